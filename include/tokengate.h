@@ -1,0 +1,239 @@
+/*
+ * tokengate.h -- C ABI of libtokengate.so, the MI355X (gfx950) hot path of
+ * TokenGate's gated prefill.
+ *
+ * Sources, cited by page title and section only:
+ *   [paper]  "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
+ *            with Learned Token Pruning" (paper page on thelatestinai.com),
+ *            Abstract and Figure 1 (a)-(c).
+ *   [aitu]   The aitualizate.com news article on TokenGate, sections
+ *            "2. Una red MLP aprende qué tokens conservar", "3. Las capas
+ *            superiores procesan únicamente los tokens seleccionados",
+ *            "Cómo consigue entrenar una selección top-K" and "Cómo identifica
+ *            el contenido que puede podarse".
+ *
+ * The path, per prompt:  gate score (all N tokens) -> top-K select (question
+ * tail always kept) -> gather of the kept rows, gate values and positions ->
+ * per upper layer: RoPE + compact KV cache, then token-gated causal GQA
+ * attention over the K kept tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is a DEVICE pointer unless its comment says otherwise.  The
+ *    caller allocates and owns every buffer; the library never allocates and
+ *    keeps no state besides a thread-local error message.
+ *  - Every call only enqueues work on `stream` (0 = the null stream) and returns
+ *    without synchronising.  Calls are thread-safe; calls on different streams
+ *    may run concurrently if their output buffers do not overlap.
+ *  - Arguments are validated on the host before any HIP call.  A failed check
+ *    returns TG_ERR_INVALID_ARG or TG_ERR_UNSUPPORTED, enqueues nothing and sets
+ *    the message returned by tg_last_error().  A launch failure reported by HIP
+ *    returns TG_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *    synchronisation.
+ *  - n == 0 (nothing to do) returns TG_OK and enqueues nothing.
+ *  - Dense tensors are contiguous and row-major in the shapes given; bf16 is
+ *    IEEE bfloat16 stored in 2 bytes; every fp32 -> bf16 conversion rounds to
+ *    nearest even.  Tensor pointers must be 16-byte aligned.
+ *  - Gate values g are fp32.  Indices and positions are int32.
+ */
+#ifndef TOKENGATE_H_
+#define TOKENGATE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_API __attribute__((visibility("default")))
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, inconsistent sizes */
+  TG_ERR_UNSUPPORTED = 2, /* valid request that this build has no kernel for */
+  TG_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} tg_status;
+
+typedef enum tg_dtype {
+  TG_FP32 = 0,
+  TG_BF16 = 1
+} tg_dtype;
+
+/* Version of this ABI; bumped on any incompatible change. */
+#define TG_ABI_VERSION 1
+TG_API int tg_abi_version(void);
+
+/* Static text for a status code ("TG_OK", ...). Never NULL. */
+TG_API const char* tg_status_string(int status);
+
+/* Detail of the last failing call made on this thread ("" if none). The
+ * pointer stays valid until the next call on this thread. */
+TG_API const char* tg_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Stage 1 -- gate MLP.  [paper] Figure 1(b): a small scoring network scores
+ * every hidden state; [aitu] section 2: the network reads each token's
+ * post-attention residual state at the selection layer L.  This library's
+ * reading of the network:
+ *     a = W1 h_j + b1  (d -> hidden),  z = SiLU(a) = a * sigmoid(a),
+ *     s_j = w2 . z + b2,               g_j = sigmoid(s_j)  in (0, 1).
+ *
+ *   dtype   TG_BF16: h and w1 are bf16, products accumulate in fp32 (MFMA) and
+ *           the epilogue (bias, SiLU, w2 dot, sigmoid) runs in fp32.
+ *           TG_FP32: h and w1 are fp32, all arithmetic fp32.
+ *   n       tokens (rows of h), >= 0.
+ *   d       hidden size.  bf16: multiple of 64.  fp32: multiple of 4.
+ *   hidden  gate MLP width.  bf16: 64, 128 or 256.  fp32: 1..1024.
+ *   h       [n, ld_h] rows; only the first d columns are read.  ld_h >= d, and
+ *           ld_h * element size must be a multiple of 16 bytes.
+ *   w1      [hidden, d] (nn.Linear layout: row k is unit k's input weights).
+ *   b1      [hidden] fp32, or NULL for zero.
+ *   w2      [hidden] fp32.
+ *   b2      output bias.
+ *   g       [n] fp32 output: gate values.
+ *   s       [n] fp32 output: scores (pre-sigmoid), or NULL.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
+                               const void* h, int64_t ld_h, const void* w1,
+                               const float* b1, const float* w2, float b2,
+                               float* g, float* s, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 2 -- top-K selection.  [paper] Figure 1(a),(b): a top-K selector at
+ * layer L keeps K of the N tokens; [aitu] sections 3 and "Cómo identifica el
+ * contenido que puede podarse": only the document may be pruned, the question
+ * is never removed, and the budget is the maximum number of kept tokens.
+ * This library's reading (exact, one correct answer):
+ *   - K counts every kept token, question included: kept = min(k, n), of which
+ *     the q_len trailing tokens [n - q_len, n) are always kept and
+ *     kd = min(k, n) - q_len are chosen among the document [0, n - q_len).
+ *   - Document tokens are ranked by g as fp32 numbers, larger first, ties to
+ *     the lower index; -0 equals +0; NaN ranks below every number.
+ *   - idx receives the kept indices in ascending order (the tail last).
+ *   - k >= n keeps every token (idx = 0..n-1).
+ *
+ *   g      [n] fp32 gate values.
+ *   n      tokens, 0 <= n < 2^31.
+ *   k      budget, >= q_len.      q_len  0 <= q_len <= min(k, n).
+ *   idx    [min(k, n)] int32 output.
+ * Errors: q_len > min(k, n), negative sizes, NULL pointers -> INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_len,
+                                int32_t* idx, hipStream_t stream);
+
+/* Ragged batch of prompts packed along the token axis.
+ *   g           [total] fp32, prompt b occupies [cu_seqlens[b], cu_seqlens[b+1]).
+ *   cu_seqlens  [batch + 1] int32 (device), non-decreasing, cu_seqlens[0] = 0.
+ *   q_lens      [batch] int32 (device); 0 <= q_lens[b] <= min(k, N_b).
+ *   batch       number of prompts, >= 0.
+ *   max_seqlen  host-side upper bound of every N_b (chooses the kernel).
+ *   k           per-prompt budget.
+ *   idx_local   [sum_b min(k, N_b)] int32 output: prompt b's kept positions,
+ *               relative to its start, at offset cu_kept[b].
+ *   cu_kept     [batch + 1] int32 output: offsets of each prompt's kept tokens.
+ * A prompt whose q_len is out of range, or whose length exceeds max_seqlen,
+ * gets -1 in every one of its idx_local entries. */
+TG_API tg_status tg_select_topk_varlen(const float* g, const int32_t* cu_seqlens,
+                                       const int32_t* q_lens, int32_t batch,
+                                       int64_t max_seqlen, int64_t k, int32_t* idx_local,
+                                       int32_t* cu_kept, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 3 -- gather.  [paper] Figure 1(b): the selector forwards the kept
+ * hidden states together with their importance scores; [aitu] section 3:
+ * the layers above L receive only the kept tokens.  Each kept token also
+ * carries its original position (its index in the prompt).
+ *   h_out[i] = h[idx[i]],  g_out[i] = g[idx[i]],  pos_out[i] = idx[i].
+ *
+ *   n          rows of h (idx entries must lie in [0, n)).
+ *   n_kept     entries of idx.
+ *   d          row length in elements; d * element size multiple of 16 bytes.
+ *   h          [n, ld_h]; h_out [n_kept, d] contiguous.
+ *   g, g_out   fp32, or both NULL to skip.   pos_out int32 [n_kept] or NULL.
+ * An idx entry outside [0, n) yields a zero row, g_out = 0 and pos_out = -1.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_gather(tg_dtype dtype, int64_t n, int64_t n_kept, int32_t d,
+                           const int32_t* idx, const void* h, int64_t ld_h,
+                           const float* g, void* h_out, float* g_out, int32_t* pos_out,
+                           hipStream_t stream);
+
+/* Packed-batch gather: prompt b's kept rows are h[cu_seqlens[b] + idx_local[i]]
+ * for i in [cu_kept[b], cu_kept[b+1]); pos_out = idx_local (positions within
+ * the prompt).  max_kept bounds every prompt's kept count (host side).  An
+ * entry outside its prompt yields a zero row, g_out = 0 and pos_out = -1. */
+TG_API tg_status tg_gather_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
+                                  const int32_t* cu_kept, int32_t batch, int64_t max_kept,
+                                  int32_t d, const int32_t* idx_local, const void* h,
+                                  int64_t ld_h, const float* g, void* h_out, float* g_out,
+                                  int32_t* pos_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 5 -- RoPE at original positions and a KV cache for kept tokens only.
+ * [aitu] section 3: discarded tokens create no key/value cache entries in the
+ * layers above L.  Position encoding is not on the pages; this library uses
+ * the rotate-half form (pairs (i, i + dh/2)) with angle pos * base^(-2i/dh).
+ *
+ * tg_rope_table fills cos_sin [max_pos, dh] fp32: row p holds
+ * cos(p*theta_0..theta_{dh/2-1}) then sin(...), computed in fp64 on the device.
+ *
+ * tg_rope_kv, per kept token i at position pos[i]:
+ *   q[i]        rotated in place             q [n_kept, hq, dh]
+ *   k_cache[i]  = rotated k[i]               k, k_cache [n_kept, hkv, dh]
+ *   v_cache[i]  = v[i]  (copy; skipped when v_cache == v)
+ * dh: a multiple of 16, at most 256.  A position outside [0, max_pos) gives
+ * zero outputs for that token.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_rope_table(float* cos_sin, int64_t max_pos, int32_t dh, double base,
+                               hipStream_t stream);
+
+TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv,
+                            int32_t dh, const int32_t* pos, const float* cos_sin,
+                            int64_t max_pos, void* q, const void* k, const void* v,
+                            void* k_cache, void* v_cache, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 4 -- token-gated causal GQA attention over the kept tokens.
+ * [paper] Figure 1(c): each attention weight is multiplied by its key's gate
+ * value g_j (the weights are then renormalised); [paper] Abstract and [aitu]
+ * "Cómo consigue entrenar una selección top-K": the importance score acts as a
+ * bias on the attention logits.  Computed form, for query head h (KV head
+ * h / (hq/hkv)) and kept query i:
+ *   o_i = sum_{j: pos_j <= pos_i} softmax_j(scale * q_i.k_j + ln max(g_j, FLT_MIN)) v_j
+ *   lse_i = ln sum_{j: pos_j <= pos_i} exp(scale * q_i.k_j + ln max(g_j, FLT_MIN))
+ * Gain 1 and temperature 1 (the pages' raw-bias form).
+ *
+ *   dtype   TG_BF16: bf16 q/k/v/o, MFMA products with fp32 accumulation and an
+ *           fp32 softmax.  TG_FP32: fp32 throughout.
+ *   n_kept  kept tokens (rows of q, k, v).
+ *   hq,hkv  heads; hq % hkv == 0.     dh: 64 or 128.
+ *   scale   logit scale (1/sqrt(dh) for the standard form); must be > 0.
+ *   q       [n_kept, hq, dh] (rotated); k, v [n_kept, hkv, dh] (the cache).
+ *   g       [n_kept] fp32 gate values of the kept tokens.
+ *   pos     [n_kept] int32 original positions, strictly increasing (the
+ *           order select + gather produce).  Precondition, not checked.
+ *   o       [n_kept, hq, dh] output, dtype.
+ *   lse     [hq, n_kept] fp32 output (natural log), or NULL.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv,
+                               int32_t dh, float scale, const void* q, const void* k,
+                               const void* v, const float* g, const int32_t* pos, void* o,
+                               float* lse, hipStream_t stream);
+
+/* Packed ragged batch: prompt b owns rows [cu_seqlens[b], cu_seqlens[b+1]) of
+ * q, k, v, g, pos, o, and columns of lse [hq, total]; prompts never attend to
+ * each other.  max_seqlen (host) bounds every prompt's row count; total is
+ * the number of packed rows.  pos holds positions within each prompt. */
+TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
+                                      int32_t batch, int64_t max_seqlen, int64_t total,
+                                      int32_t hq, int32_t hkv, int32_t dh, float scale,
+                                      const void* q, const void* k, const void* v,
+                                      const float* g, const int32_t* pos, void* o,
+                                      float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H_ */

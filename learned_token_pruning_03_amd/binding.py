@@ -1,0 +1,264 @@
+"""Thin ctypes binding over libtokengate.so (include/tokengate.h).
+
+Functions carry the C names.  They take torch tensors that live on the GPU,
+marshal their data pointers, sizes and torch's current HIP stream, and call
+the C ABI; every step of the computation runs in the library's HIP kernels.
+PyTorch is used only to own device memory and to provide the stream.  Output
+tensors may be passed in (no allocation) or are allocated here with
+``torch.empty`` on the input's device.  A missing library raises; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtokengate.so")
+
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
+TG_FP32, TG_BF16 = 0, 1
+
+_c_vp = ctypes.c_void_p
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_f32 = ctypes.c_float
+_c_f64 = ctypes.c_double
+
+# name -> (argtypes, restype)
+SIGNATURES = {
+    "tg_abi_version": ([], ctypes.c_int),
+    "tg_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "tg_last_error": ([], ctypes.c_char_p),
+    "tg_gate_score": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32,
+                       _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_select_topk": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
+    "tg_select_topk_varlen": ([_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+                              ctypes.c_int),
+    "tg_gather": ([ctypes.c_int, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
+                   _c_vp], ctypes.c_int),
+    "tg_gather_varlen": ([ctypes.c_int, _c_vp, _c_vp, _c_i32, _c_i64, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp,
+                          _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_rope_table": ([_c_vp, _c_i64, _c_i32, _c_f64, _c_vp], ctypes.c_int),
+    "tg_rope_kv": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
+                    _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_gated_attn": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                       _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_gated_attn_varlen": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32,
+                              _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, func: str, status: int, detail: str):
+        super().__init__(f"{func}: {status_string(status)}: {detail}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libtokengate.so once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"libtokengate.so not found at {path}; build it with "
+                           "`python -m learned_token_pruning_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (argtypes, restype) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tg_status_string(status).decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != TG_OK:
+        raise TokenGateError(func, status, load_library().tg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> Optional[int]:
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    if t.dtype == torch.float32:
+        return TG_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+# ---------------------------------------------------------------------------
+def tg_gate_score(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                  b2: float, g: Optional[torch.Tensor] = None, s: Optional[torch.Tensor] = None,
+                  want_scores: bool = False):
+    """g [n] fp32 (and s [n] if requested) for h [n, d], W1 [hidden, d]."""
+    lib = load_library()
+    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
+    n, d = h.shape
+    hidden = w1.shape[0]
+    _need(w1.shape == (hidden, d) and w1.is_contiguous() and w1.dtype == h.dtype, "w1 must be [hidden, d]")
+    _need(w2.numel() == hidden and w2.dtype == torch.float32, "w2 must be fp32 [hidden]")
+    _need(b1 is None or (b1.numel() == hidden and b1.dtype == torch.float32), "b1 must be fp32 [hidden]")
+    if g is None:
+        g = torch.empty(n, dtype=torch.float32, device=h.device)
+    if want_scores and s is None:
+        s = torch.empty(n, dtype=torch.float32, device=h.device)
+    _check("tg_gate_score", lib.tg_gate_score(_dtype_code(h), n, d, hidden, _ptr(h), h.stride(0), _ptr(w1),
+                                              _ptr(b1), _ptr(w2), float(b2), _ptr(g), _ptr(s), _stream(h)))
+    return (g, s) if want_scores or s is not None else g
+
+
+def tg_select_topk(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tensor] = None):
+    """Ascending int32 indices of the min(k, n) kept tokens."""
+    lib = load_library()
+    _need(g.dim() == 1 and g.dtype == torch.float32 and g.is_contiguous(), "g must be contiguous fp32 [n]")
+    n = g.shape[0]
+    kept = min(int(k), n)
+    if idx is None:
+        idx = torch.empty(kept, dtype=torch.int32, device=g.device)
+    _need(idx.numel() >= kept and idx.dtype == torch.int32, "idx must be int32 with min(k, n) entries")
+    _check("tg_select_topk", lib.tg_select_topk(_ptr(g), n, int(k), int(q_len), _ptr(idx), _stream(g)))
+    return idx
+
+
+def tg_select_topk_varlen(g: torch.Tensor, cu_seqlens: torch.Tensor, q_lens: torch.Tensor, max_seqlen: int,
+                          k: int, total_kept: int, idx_local: Optional[torch.Tensor] = None,
+                          cu_kept: Optional[torch.Tensor] = None):
+    """Per-prompt selection over a packed score vector; returns (idx_local, cu_kept)."""
+    lib = load_library()
+    batch = cu_seqlens.numel() - 1
+    _need(cu_seqlens.dtype == torch.int32 and q_lens.dtype == torch.int32, "cu_seqlens and q_lens are int32")
+    if idx_local is None:
+        idx_local = torch.empty(max(total_kept, 1), dtype=torch.int32, device=g.device)
+    if cu_kept is None:
+        cu_kept = torch.empty(batch + 1, dtype=torch.int32, device=g.device)
+    _check("tg_select_topk_varlen",
+           lib.tg_select_topk_varlen(_ptr(g), _ptr(cu_seqlens), _ptr(q_lens), batch, int(max_seqlen), int(k),
+                                     _ptr(idx_local), _ptr(cu_kept), _stream(g)))
+    return idx_local[:total_kept], cu_kept
+
+
+def tg_gather(h: torch.Tensor, g: Optional[torch.Tensor], idx: torch.Tensor, h_out: Optional[torch.Tensor] = None,
+              g_out: Optional[torch.Tensor] = None, pos_out: Optional[torch.Tensor] = None):
+    """(h[idx], g[idx], idx) as new tensors (or into the given ones)."""
+    lib = load_library()
+    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
+    n, d = h.shape
+    nk = idx.numel()
+    if h_out is None:
+        h_out = torch.empty(nk, d, dtype=h.dtype, device=h.device)
+    if g is not None and g_out is None:
+        g_out = torch.empty(nk, dtype=torch.float32, device=h.device)
+    if pos_out is None:
+        pos_out = torch.empty(nk, dtype=torch.int32, device=h.device)
+    _check("tg_gather", lib.tg_gather(_dtype_code(h), n, nk, d, _ptr(idx), _ptr(h), h.stride(0), _ptr(g),
+                                      _ptr(h_out), _ptr(g_out), _ptr(pos_out), _stream(h)))
+    return h_out, g_out, pos_out
+
+
+def tg_gather_varlen(h: torch.Tensor, g: Optional[torch.Tensor], idx_local: torch.Tensor, cu_seqlens: torch.Tensor,
+                     cu_kept: torch.Tensor, max_kept: int, h_out=None, g_out=None, pos_out=None):
+    lib = load_library()
+    n, d = h.shape
+    nk = idx_local.numel()
+    batch = cu_seqlens.numel() - 1
+    if h_out is None:
+        h_out = torch.empty(nk, d, dtype=h.dtype, device=h.device)
+    if g is not None and g_out is None:
+        g_out = torch.empty(nk, dtype=torch.float32, device=h.device)
+    if pos_out is None:
+        pos_out = torch.empty(nk, dtype=torch.int32, device=h.device)
+    _check("tg_gather_varlen",
+           lib.tg_gather_varlen(_dtype_code(h), _ptr(cu_seqlens), _ptr(cu_kept), batch, int(max_kept), d,
+                                _ptr(idx_local), _ptr(h), h.stride(0), _ptr(g), _ptr(h_out), _ptr(g_out),
+                                _ptr(pos_out), _stream(h)))
+    return h_out, g_out, pos_out
+
+
+def tg_rope_table(max_pos: int, dh: int, base: float, device, out: Optional[torch.Tensor] = None):
+    """cos/sin table [max_pos, dh] fp32 (cos | sin halves), built on the device in fp64."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(max_pos, dh, dtype=torch.float32, device=device)
+    _check("tg_rope_table", lib.tg_rope_table(_ptr(out), int(max_pos), int(dh), float(base), _stream(out)))
+    return out
+
+
+def tg_rope_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor,
+               k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None):
+    """Rotates q in place; returns (q, k_cache, v_cache)."""
+    lib = load_library()
+    n, hq, dh = q.shape
+    hkv = k.shape[1]
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(k.shape == (n, hkv, dh) and v.shape == (n, hkv, dh), "k and v must be [n, hkv, dh]")
+    if k_cache is None:
+        k_cache = torch.empty_like(k)
+    if v_cache is None:
+        v_cache = torch.empty_like(v)
+    _check("tg_rope_kv", lib.tg_rope_kv(_dtype_code(q), n, hq, hkv, dh, _ptr(pos), _ptr(cos_sin),
+                                        cos_sin.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
+                                        _ptr(v_cache), _stream(q)))
+    return q, k_cache, v_cache
+
+
+def tg_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, pos: torch.Tensor,
+                  scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = False):
+    """Token-gated causal GQA attention; returns o (and lse [hq, n] if requested)."""
+    lib = load_library()
+    n, hq, dh = q.shape
+    hkv = k.shape[1]
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(g.dtype == torch.float32 and pos.dtype == torch.int32, "g is fp32 and pos int32")
+    if scale is None:
+        scale = dh ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(hq, n, dtype=torch.float32, device=q.device)
+    _check("tg_gated_attn", lib.tg_gated_attn(_dtype_code(q), n, hq, hkv, dh, float(scale), _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(g), _ptr(pos), _ptr(o), _ptr(lse), _stream(q)))
+    return (o, lse) if (want_lse or lse is not None) else o
+
+
+def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, pos: torch.Tensor,
+                         cu_seqlens: torch.Tensor, max_seqlen: int, scale: Optional[float] = None,
+                         o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         want_lse: bool = False):
+    lib = load_library()
+    total, hq, dh = q.shape
+    hkv = k.shape[1]
+    batch = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = dh ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(hq, total, dtype=torch.float32, device=q.device)
+    _check("tg_gated_attn_varlen",
+           lib.tg_gated_attn_varlen(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv, dh,
+                                    float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(pos), _ptr(o), _ptr(lse),
+                                    _stream(q)))
+    return (o, lse) if (want_lse or lse is not None) else o

@@ -1,0 +1,255 @@
+// Host side of the C ABI declared in include/tokengate.h: argument validation
+// (before any HIP call), dispatch to the kernel launchers, error reporting.
+#include "tokengate.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tg_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+tg_status fail(tg_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tg_status ok() {
+  g_last_error[0] = '\0';
+  return TG_OK;
+}
+
+tg_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    return fail(TG_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(tg_dtype dt) { return dt == TG_BF16 ? 2 : 4; }
+
+bool valid_dtype(tg_dtype dt) { return dt == TG_BF16 || dt == TG_FP32; }
+
+constexpr int64_t kMaxI32 = 2147483647LL;
+
+}  // namespace
+
+extern "C" {
+
+TG_API int tg_abi_version(void) { return TG_ABI_VERSION; }
+
+TG_API const char* tg_status_string(int status) {
+  switch (status) {
+    case TG_OK: return "TG_OK";
+    case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG";
+    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
+    case TG_ERR_HIP: return "TG_ERR_HIP";
+    default: return "TG_UNKNOWN_STATUS";
+  }
+}
+
+TG_API const char* tg_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------------------
+TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
+                               const void* h, int64_t ld_h, const void* w1, const float* b1,
+                               const float* w2, float b2, float* g, float* s,
+                               hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "gate: unknown dtype %d", (int)dtype);
+  if (n < 0 || n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "gate: n=%lld out of range", (long long)n);
+  if (d <= 0 || hidden <= 0) return fail(TG_ERR_INVALID_ARG, "gate: d and hidden must be positive");
+  if (ld_h < d) return fail(TG_ERR_INVALID_ARG, "gate: ld_h=%lld < d=%d", (long long)ld_h, d);
+  const int es = elem_size(dtype);
+  if ((ld_h * es) % 16 != 0) return fail(TG_ERR_INVALID_ARG, "gate: ld_h*elem_size must be a multiple of 16 bytes");
+  if (dtype == TG_BF16) {
+    if (d % 64 != 0) return fail(TG_ERR_UNSUPPORTED, "gate bf16: d=%d must be a multiple of 64", d);
+    if (hidden != 64 && hidden != 128 && hidden != 256)
+      return fail(TG_ERR_UNSUPPORTED, "gate bf16: hidden=%d must be 64, 128 or 256", hidden);
+  } else {
+    if (d % 4 != 0) return fail(TG_ERR_UNSUPPORTED, "gate fp32: d=%d must be a multiple of 4", d);
+    if (hidden > 1024) return fail(TG_ERR_UNSUPPORTED, "gate fp32: hidden=%d > 1024", hidden);
+  }
+  if (n == 0) return ok();
+  if (!h || !w1 || !w2 || !g) return fail(TG_ERR_INVALID_ARG, "gate: NULL h, w1, w2 or g");
+  if (!aligned16(h) || !aligned16(w1)) return fail(TG_ERR_INVALID_ARG, "gate: h and w1 must be 16-byte aligned");
+  hipError_t e;
+  if (dtype == TG_BF16)
+    e = tg::launch_gate_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
+  else
+    e = tg::launch_gate_f32(n, d, hidden, static_cast<const float*>(h), ld_h,
+                            static_cast<const float*>(w1), b1, w2, b2, g, s, stream);
+  return from_hip(e, "gate");
+}
+
+// ---------------------------------------------------------------------------
+TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_len,
+                                int32_t* idx, hipStream_t stream) {
+  if (n < 0 || n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "select: n=%lld out of range", (long long)n);
+  if (k < 0) return fail(TG_ERR_INVALID_ARG, "select: k=%lld < 0", (long long)k);
+  const int64_t kept = k < n ? k : n;
+  if (q_len < 0 || q_len > kept)
+    return fail(TG_ERR_INVALID_ARG, "select: q_len=%lld outside [0, min(k, n)=%lld]", (long long)q_len,
+                (long long)kept);
+  if (n == 0) return ok();
+  if (!g || !idx) return fail(TG_ERR_INVALID_ARG, "select: NULL g or idx");
+  return from_hip(tg::launch_select(g, n, k, q_len, nullptr, nullptr, 1, n, idx, nullptr, stream),
+                  "select");
+}
+
+TG_API tg_status tg_select_topk_varlen(const float* g, const int32_t* cu_seqlens,
+                                       const int32_t* q_lens, int32_t batch, int64_t max_seqlen,
+                                       int64_t k, int32_t* idx_local, int32_t* cu_kept,
+                                       hipStream_t stream) {
+  if (batch < 0) return fail(TG_ERR_INVALID_ARG, "select_varlen: batch < 0");
+  if (max_seqlen < 0 || max_seqlen > kMaxI32) return fail(TG_ERR_INVALID_ARG, "select_varlen: max_seqlen out of range");
+  if (k < 0) return fail(TG_ERR_INVALID_ARG, "select_varlen: k < 0");
+  if (batch == 0) return ok();
+  if (!g || !cu_seqlens || !q_lens || !idx_local || !cu_kept)
+    return fail(TG_ERR_INVALID_ARG, "select_varlen: NULL pointer argument");
+  return from_hip(tg::launch_select(g, 0, k, 0, cu_seqlens, q_lens, batch, max_seqlen, idx_local,
+                                    cu_kept, stream),
+                  "select_varlen");
+}
+
+// ---------------------------------------------------------------------------
+static tg_status check_gather_common(tg_dtype dtype, int32_t d, const void* h, int64_t ld_h,
+                                     const float* g, void* h_out, float* g_out) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "gather: unknown dtype %d", (int)dtype);
+  const int es = elem_size(dtype);
+  if (d <= 0) return fail(TG_ERR_INVALID_ARG, "gather: d must be positive");
+  if ((int64_t)d * es % 16 != 0) return fail(TG_ERR_UNSUPPORTED, "gather: d*elem_size must be a multiple of 16 bytes");
+  if (ld_h < d || (ld_h * es) % 16 != 0) return fail(TG_ERR_INVALID_ARG, "gather: ld_h must be >= d with 16-byte rows");
+  if ((g == nullptr) != (g_out == nullptr)) return fail(TG_ERR_INVALID_ARG, "gather: pass both g and g_out, or neither");
+  if (!h || !h_out) return fail(TG_ERR_INVALID_ARG, "gather: NULL h or h_out");
+  if (!aligned16(h) || !aligned16(h_out)) return fail(TG_ERR_INVALID_ARG, "gather: h and h_out must be 16-byte aligned");
+  return TG_OK;
+}
+
+TG_API tg_status tg_gather(tg_dtype dtype, int64_t n, int64_t n_kept, int32_t d, const int32_t* idx,
+                           const void* h, int64_t ld_h, const float* g, void* h_out, float* g_out,
+                           int32_t* pos_out, hipStream_t stream) {
+  if (n < 0 || n > kMaxI32 || n_kept < 0 || n_kept > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "gather: n or n_kept out of range");
+  if (n_kept == 0) return ok();
+  tg_status st = check_gather_common(dtype, d, h, ld_h, g, h_out, g_out);
+  if (st != TG_OK) return st;
+  if (!idx) return fail(TG_ERR_INVALID_ARG, "gather: NULL idx");
+  return from_hip(tg::launch_gather(elem_size(dtype), n, n_kept, d, idx, h, ld_h, g, h_out, g_out,
+                                    pos_out, nullptr, nullptr, 1, n_kept, stream),
+                  "gather");
+}
+
+TG_API tg_status tg_gather_varlen(tg_dtype dtype, const int32_t* cu_seqlens, const int32_t* cu_kept,
+                                  int32_t batch, int64_t max_kept, int32_t d,
+                                  const int32_t* idx_local, const void* h, int64_t ld_h,
+                                  const float* g, void* h_out, float* g_out, int32_t* pos_out,
+                                  hipStream_t stream) {
+  if (batch < 0 || max_kept < 0 || max_kept > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "gather_varlen: batch or max_kept out of range");
+  if (batch == 0 || max_kept == 0) return ok();
+  tg_status st = check_gather_common(dtype, d, h, ld_h, g, h_out, g_out);
+  if (st != TG_OK) return st;
+  if (!idx_local || !cu_seqlens || !cu_kept) return fail(TG_ERR_INVALID_ARG, "gather_varlen: NULL pointer argument");
+  return from_hip(tg::launch_gather(elem_size(dtype), 0, 0, d, idx_local, h, ld_h, g, h_out, g_out,
+                                    pos_out, cu_seqlens, cu_kept, batch, max_kept, stream),
+                  "gather_varlen");
+}
+
+// ---------------------------------------------------------------------------
+TG_API tg_status tg_rope_table(float* cos_sin, int64_t max_pos, int32_t dh, double base,
+                               hipStream_t stream) {
+  if (max_pos < 0 || max_pos > kMaxI32) return fail(TG_ERR_INVALID_ARG, "rope_table: max_pos out of range");
+  if (dh <= 0 || dh % 2 != 0 || dh > 256) return fail(TG_ERR_INVALID_ARG, "rope_table: dh must be even and <= 256");
+  if (!(base > 1.0)) return fail(TG_ERR_INVALID_ARG, "rope_table: base must be > 1");
+  if (max_pos == 0) return ok();
+  if (!cos_sin) return fail(TG_ERR_INVALID_ARG, "rope_table: NULL cos_sin");
+  return from_hip(tg::launch_rope_table(cos_sin, max_pos, dh, base, stream), "rope_table");
+}
+
+TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv, int32_t dh,
+                            const int32_t* pos, const float* cos_sin, int64_t max_pos, void* q,
+                            const void* k, const void* v, void* k_cache, void* v_cache,
+                            hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "rope_kv: unknown dtype %d", (int)dtype);
+  if (n_kept < 0 || n_kept > kMaxI32 || max_pos < 0 || max_pos > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "rope_kv: n_kept or max_pos out of range");
+  if (hq <= 0 || hkv <= 0) return fail(TG_ERR_INVALID_ARG, "rope_kv: head counts must be positive");
+  if (dh <= 0 || dh % 16 != 0 || dh > 256) return fail(TG_ERR_UNSUPPORTED, "rope_kv: dh=%d must be a multiple of 16, <= 256", dh);
+  if (n_kept == 0) return ok();
+  if (!pos || !cos_sin || !q || !k || !v || !k_cache || !v_cache)
+    return fail(TG_ERR_INVALID_ARG, "rope_kv: NULL pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(cos_sin))
+    return fail(TG_ERR_INVALID_ARG, "rope_kv: tensors must be 16-byte aligned");
+  return from_hip(tg::launch_rope_kv(elem_size(dtype), n_kept, hq, hkv, dh, pos, cos_sin, max_pos, q, k,
+                                     v, k_cache, v_cache, stream),
+                  "rope_kv");
+}
+
+// ---------------------------------------------------------------------------
+static tg_status check_attn(tg_dtype dtype, int32_t hq, int32_t hkv, int32_t dh, float scale,
+                            const void* q, const void* k, const void* v, const float* g,
+                            const int32_t* pos, void* o) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "attn: unknown dtype %d", (int)dtype);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(TG_ERR_INVALID_ARG, "attn: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "attn: dh=%d must be 64 or 128", dh);
+  if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "attn: scale must be > 0");
+  if (!q || !k || !v || !g || !pos || !o) return fail(TG_ERR_INVALID_ARG, "attn: NULL pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(TG_ERR_INVALID_ARG, "attn: q, k, v and o must be 16-byte aligned");
+  return TG_OK;
+}
+
+static hipError_t dispatch_attn(tg_dtype dtype, int64_t total, const int32_t* cu, int batch,
+                                int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const int32_t* pos, void* o, float* lse, hipStream_t stream) {
+  if (dtype == TG_BF16)
+    return tg::launch_attn_bf16(total, cu, batch, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o,
+                                lse, stream);
+  return tg::launch_attn_f32(total, cu, batch, max_seqlen, hq, hkv, dh, scale,
+                             static_cast<const float*>(q), static_cast<const float*>(k),
+                             static_cast<const float*>(v), g, pos, static_cast<float*>(o), lse,
+                             stream);
+}
+
+TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv, int32_t dh,
+                               float scale, const void* q, const void* k, const void* v,
+                               const float* g, const int32_t* pos, void* o, float* lse,
+                               hipStream_t stream) {
+  if (n_kept < 0 || n_kept > kMaxI32) return fail(TG_ERR_INVALID_ARG, "attn: n_kept out of range");
+  if (n_kept == 0) return ok();
+  tg_status st = check_attn(dtype, hq, hkv, dh, scale, q, k, v, g, pos, o);
+  if (st != TG_OK) return st;
+  return from_hip(dispatch_attn(dtype, n_kept, nullptr, 1, n_kept, hq, hkv, dh, scale, q, k, v, g, pos,
+                                o, lse, stream),
+                  "attn");
+}
+
+TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                      int64_t max_seqlen, int64_t total, int32_t hq, int32_t hkv,
+                                      int32_t dh, float scale, const void* q, const void* k,
+                                      const void* v, const float* g, const int32_t* pos, void* o,
+                                      float* lse, hipStream_t stream) {
+  if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32 || total < 0 || total > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "attn_varlen: batch, max_seqlen or total out of range");
+  if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
+  tg_status st = check_attn(dtype, hq, hkv, dh, scale, q, k, v, g, pos, o);
+  if (st != TG_OK) return st;
+  if (!cu_seqlens) return fail(TG_ERR_INVALID_ARG, "attn_varlen: NULL cu_seqlens");
+  return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
+                                g, pos, o, lse, stream),
+                  "attn_varlen");
+}
+
+}  // extern "C"

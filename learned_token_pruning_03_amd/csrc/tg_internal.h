@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libtokengate.
+// Not part of the public ABI (see include/tokengate.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+// ---- vector types used with the gfx950 MFMA builtins ----------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kFltMin = 1.17549435e-38f;  // smallest normal fp32, 2^-126
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- launchers (defined in the kernel translation units) -------------------
+hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
+                            const void* w1, const float* b1, const float* w2, float b2,
+                            float* g, float* s, hipStream_t stream);
+hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,
+                           const float* w1, const float* b1, const float* w2, float b2,
+                           float* g, float* s, hipStream_t stream);
+
+hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len,
+                         const int32_t* cu_seqlens, const int32_t* q_lens, int batch,
+                         int64_t max_seqlen, int32_t* idx, int32_t* cu_kept,
+                         hipStream_t stream);
+
+hipError_t launch_gather(int elem_bytes, int64_t n, int64_t n_kept, int d, const int32_t* idx,
+                         const void* h, int64_t ld_h, const float* g, void* h_out,
+                         float* g_out, int32_t* pos_out, const int32_t* cu_seqlens,
+                         const int32_t* cu_kept, int batch, int64_t max_kept,
+                         hipStream_t stream);
+
+hipError_t launch_rope_table(float* cos_sin, int64_t max_pos, int dh, double base,
+                             hipStream_t stream);
+hipError_t launch_rope_kv(int elem_bytes, int64_t n_kept, int hq, int hkv, int dh,
+                          const int32_t* pos, const float* cos_sin, int64_t max_pos, void* q,
+                          const void* k, const void* v, void* k_cache, void* v_cache,
+                          hipStream_t stream);
+
+hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
+                            int64_t max_seqlen, int hq, int hkv, int dh, float scale,
+                            const void* q, const void* k, const void* v, const float* g,
+                            const int32_t* pos, void* o, float* lse, hipStream_t stream);
+hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
+                           int64_t max_seqlen, int hq, int hkv, int dh, float scale,
+                           const float* q, const float* k, const float* v, const float* g,
+                           const int32_t* pos, float* o, float* lse, hipStream_t stream);
+
+}  // namespace tg

@@ -207,11 +207,13 @@ def ref_rope_kv(q, k, v, pos, base: float):
 # the bias stays finite; key j is visible to query i iff pos_j <= pos_i; query
 # head h uses KV head h // (Hq / Hkv).
 # --------------------------------------------------------------------------
-def ref_attn(q, k, v, g, pos, scale: float | None = None):
+def ref_attn(q, k, v, g, pos, scale: float | None = None, rows=None):
     """q [n, hq, dh], k/v [n, hkv, dh], g [n], pos [n].
 
     Returns (o [n, hq, dh], lse [hq, n]) in float64; lse is the natural-log
-    normaliser of the biased logits.
+    normaliser of the biased logits.  With ``rows`` (query indices) only those
+    queries are computed, against all n keys: o [len(rows), hq, dh] and
+    lse [hq, len(rows)].
     """
     q = _f64(q)
     k = _f64(k)
@@ -220,16 +222,17 @@ def ref_attn(q, k, v, g, pos, scale: float | None = None):
     pos = _i64(pos)
     n, hq, dh = q.shape
     hkv = k.shape[1]
+    rows = np.arange(n) if rows is None else _i64(rows)
     if scale is None:
         scale = 1.0 / np.sqrt(dh)
     group = hq // hkv
     bias = np.log(np.maximum(g, FLT_MIN))                     # [n]
-    visible = pos[None, :] <= pos[:, None]                    # [query i, key j]
-    o = np.empty((n, hq, dh))
-    lse = np.empty((hq, n))
+    visible = pos[None, :] <= pos[rows][:, None]              # [query i, key j]
+    o = np.empty((len(rows), hq, dh))
+    lse = np.empty((hq, len(rows)))
     for h in range(hq):
         kvh = h // group
-        s = scale * (q[:, h, :] @ k[:, kvh, :].T) + bias[None, :]
+        s = scale * (q[rows, h, :] @ k[:, kvh, :].T) + bias[None, :]
         s = np.where(visible, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)

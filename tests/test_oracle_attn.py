@@ -126,3 +126,12 @@ def test_attn_varlen_is_per_prompt():
         ob, lb = ref_attn(q[a:e], k[a:e], v[a:e], g[a:e], pos[a:e])
         np.testing.assert_array_equal(o[a:e], ob)
         np.testing.assert_array_equal(lse[:, a:e], lb)
+
+
+def test_attn_row_subset_equals_full_rows():
+    q, k, v, g, pos = _rand(10, n=40)
+    o, lse = ref_attn(q, k, v, g, pos)
+    rows = np.array([0, 7, 39, 12])
+    os_, ls = ref_attn(q, k, v, g, pos, rows=rows)
+    np.testing.assert_array_equal(os_, o[rows])
+    np.testing.assert_array_equal(ls, lse[:, rows])

@@ -1,0 +1,395 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle on the same
+seeded inputs (stage by stage, each stage fed the same bytes on both sides).
+
+Bars: select and gather bit-exact; gate g within 1e-2 relative (bf16) and
+1e-5 (fp32); attention within 2e-2 max-abs (bf16, fp32 accumulation) and
+1e-4 (fp32); RoPE output within one bf16 rounding of the fp64 rotation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import learned_token_pruning_03_amd.workloads as W
+from oracle import ref_attn, ref_attn_varlen, ref_gate, ref_gather, ref_rope, ref_select, ref_select_varlen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _rel_err(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30)))
+
+
+# ----------------------------------------------------------------------------- gate
+def _gate_case(tg, n, d, hidden, dtype, seed, planted=0.0):
+    h = W.hidden_states(n, d, dtype, seed, planted_frac=planted)
+    w1, b1, w2, b2 = W.gate_weights(d, hidden, dtype, seed)
+    b1 = b1 + torch.linspace(-0.5, 0.5, hidden)  # non-zero bias exercises the b1 path
+    g_ref, s_ref = ref_gate(h, w1, b1, w2, 0.25)
+    g, s = tg.tg_gate_score(h.to(DEV), w1.to(DEV), b1.to(DEV), w2.to(DEV), 0.25, want_scores=True)
+    torch.cuda.synchronize()
+    return g.cpu().numpy(), s.cpu().numpy(), g_ref, s_ref
+
+
+def test_gate_tiny_fp32(gpu_lib):
+    sh = W.SHAPES["tiny"]
+    _say("gate tiny fp32", sh.n, sh.d, sh.hidden)
+    g, s, g_ref, s_ref = _gate_case(gpu_lib, sh.n, sh.d, sh.hidden, torch.float32, W.SEEDS["tiny"])
+    assert _rel_err(g, g_ref) <= 1e-5
+    np.testing.assert_allclose(s, s_ref, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("n,d,hidden", [(1000, 256, 64), (777, 512, 128), (300, 2048, 256), (129, 64, 256),
+                                        (1, 128, 256), (128, 192, 64)])
+def test_gate_bf16_shapes(gpu_lib, n, d, hidden):
+    _say("gate bf16", n, d, hidden)
+    g, s, g_ref, s_ref = _gate_case(gpu_lib, n, d, hidden, torch.bfloat16, 7 + n)
+    err = _rel_err(g, g_ref)
+    _say("  max rel err g", err)
+    assert err <= 1e-2
+    np.testing.assert_allclose(s, s_ref, rtol=1e-3, atol=1e-3)
+
+
+def test_gate_bf16_qwen_32k_full(gpu_lib):
+    sh = W.SHAPES["qwen1p7b_32k"]
+    _say("gate bf16 32k full", sh.n, sh.d, sh.hidden)
+    g, s, g_ref, s_ref = _gate_case(gpu_lib, sh.n, sh.d, sh.hidden, torch.bfloat16, W.SEEDS["qwen1p7b_32k"],
+                                    planted=sh.planted_frac)
+    err = _rel_err(g, g_ref)
+    _say("  max rel err g", err)
+    assert err <= 1e-2
+
+
+def test_gate_fp32_ragged(gpu_lib):
+    _say("gate fp32 ragged")
+    g, s, g_ref, s_ref = _gate_case(gpu_lib, 333, 100, 37, torch.float32, 5)
+    assert _rel_err(g, g_ref) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- select
+def _sel(tg, g_cpu, k, q):
+    idx = tg.tg_select_topk(g_cpu.to(DEV), k, q)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().astype(np.int64)
+
+
+def _score_vector(kind, n, seed):
+    if kind == "uniform":
+        return W.random_scores(n, seed)
+    if kind == "wide":
+        return W.gate_values_wide(n, seed)
+    if kind == "tie8":
+        return W.tie_storm_scores(n, 8, seed)
+    if kind == "equal":
+        return torch.full((n,), 0.5, dtype=torch.float32)
+    if kind == "saturated":
+        g = W.random_scores(n, seed)
+        g[torch.arange(n) % 3 == 0] = 1.0
+        return g
+    if kind == "special":
+        g = W.random_scores(n, seed) - 0.5
+        g[::7] = float("nan")
+        g[1::11] = -0.0
+        g[2::11] = 0.0
+        g[3::13] = float("-inf")
+        g[4::17] = float("inf")
+        return g
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "wide", "tie8", "equal", "saturated", "special"])
+@pytest.mark.parametrize("n,k,q", [(512, 128, 32), (1000, 300, 17), (5000, 999, 0), (4097, 4096, 64),
+                                   (70, 64, 64), (64, 100, 10), (3, 2, 1)])
+def test_select_bit_exact(gpu_lib, kind, n, k, q):
+    g = _score_vector(kind, n, n + k)
+    got = _sel(gpu_lib, g, k, q)
+    want = ref_select(g.numpy(), k, q)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name,n,k,q,kind", [("qwen1p7b_32k", 32768, 4096, 64, "uniform"),
+                                             ("qwen1p7b_32k", 32768, 4096, 64, "tie8"),
+                                             ("stack19", 65536, 4096, 64, "uniform"),
+                                             ("qwen1p7b_128k", 131072, 8192, 64, "wide"),
+                                             ("qwen1p7b_128k", 131072, 8192, 64, "tie8"),
+                                             ("long", 200003, 20000, 100, "uniform")])
+def test_select_full_sizes(gpu_lib, name, n, k, q, kind):
+    _say("select", name, n, k, q, kind)
+    g = _score_vector(kind, n, 3)
+    np.testing.assert_array_equal(_sel(gpu_lib, g, k, q), ref_select(g.numpy(), k, q))
+
+
+def test_select_budget_covers_prompt_and_tail_only(gpu_lib):
+    g = W.random_scores(300, 1)
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 300, 20), np.arange(300))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 1000, 20), np.arange(300))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 20, 20), np.arange(280, 300))
+
+
+def test_select_varlen_ragged_batch(gpu_lib):
+    ns, qs = W.ragged_lengths(8, W.SEEDS["ragged8"])
+    ns = ns[:6] + [100, 0]
+    qs = qs[:6] + [100, 0]
+    k = 256
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    g = W.random_scores(int(cu[-1]), 9)
+    want, want_cu = ref_select_varlen(g.numpy(), cu, qs, k)
+    idx, cu_kept = gpu_lib.tg_select_topk_varlen(g.to(DEV), torch.from_numpy(cu).to(DEV),
+                                                 torch.tensor(qs, dtype=torch.int32, device=DEV), max(ns), k,
+                                                 int(want_cu[-1]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cu_kept.cpu().numpy(), want_cu)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+# ----------------------------------------------------------------------------- gather
+@pytest.mark.parametrize("dtype,n,d,nk", [(torch.bfloat16, 1000, 2048, 333), (torch.float32, 512, 256, 128),
+                                          (torch.bfloat16, 32768, 2048, 4096), (torch.bfloat16, 50, 8, 50)])
+def test_gather_bit_exact(gpu_lib, dtype, n, d, nk):
+    _say("gather", dtype, n, d, nk)
+    h = W.hidden_states(n, d, dtype, 11)
+    g = W.random_scores(n, 12)
+    idx = torch.from_numpy(np.sort(np.random.default_rng(n).choice(n, nk, replace=False)).astype(np.int32))
+    hk, gk, pos = gpu_lib.tg_gather(h.to(DEV), g.to(DEV), idx.to(DEV))
+    torch.cuda.synchronize()
+    wh, wg, wp = ref_gather(h.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy(), g.numpy(),
+                            idx.numpy())
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy(),
+                                  wh)
+    np.testing.assert_array_equal(gk.cpu().numpy(), wg)
+    np.testing.assert_array_equal(pos.cpu().numpy(), wp)
+
+
+def test_gather_out_of_range_index_gives_zero_row(gpu_lib):
+    h = W.hidden_states(10, 64, torch.bfloat16, 1).to(DEV)
+    g = W.random_scores(10, 1).to(DEV)
+    idx = torch.tensor([3, 10, -1, 9], dtype=torch.int32, device=DEV)
+    hk, gk, pos = gpu_lib.tg_gather(h, g, idx)
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == [3, -1, -1, 9]
+    assert torch.all(hk[1:3].float() == 0).item() and gk[1].item() == 0.0
+    assert torch.equal(hk[0], h[3]) and torch.equal(hk[3], h[9])
+
+
+def test_gather_varlen(gpu_lib):
+    ns = [700, 5, 1300]
+    qs = [10, 5, 64]
+    k = 256
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    g = W.random_scores(int(cu[-1]), 4)
+    h = W.hidden_states(int(cu[-1]), 2048, torch.bfloat16, 4)
+    idx_local, cu_kept = ref_select_varlen(g.numpy(), cu, qs, k)
+    hk, gk, pos = gpu_lib.tg_gather_varlen(h.to(DEV), g.to(DEV), torch.from_numpy(idx_local.astype(np.int32)).to(DEV),
+                                           torch.from_numpy(cu).to(DEV),
+                                           torch.from_numpy(cu_kept.astype(np.int32)).to(DEV), k)
+    torch.cuda.synchronize()
+    rows = np.concatenate([cu[b] + idx_local[cu_kept[b]:cu_kept[b + 1]] for b in range(3)])
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16).numpy(), h.view(torch.int16).numpy()[rows])
+    np.testing.assert_array_equal(gk.cpu().numpy(), g.numpy()[rows])
+    np.testing.assert_array_equal(pos.cpu().numpy(), idx_local)
+
+
+# ----------------------------------------------------------------------------- rope
+@pytest.mark.parametrize("dtype,n,hq,hkv,dh", [(torch.bfloat16, 4096, 16, 8, 128), (torch.bfloat16, 77, 4, 2, 64),
+                                               (torch.float32, 128, 4, 2, 64), (torch.bfloat16, 33, 2, 1, 16)])
+def test_rope_kv_parity(gpu_lib, dtype, n, hq, hkv, dh):
+    _say("rope", dtype, n, hq, hkv, dh)
+    base = 1e6
+    max_pos = 131072
+    q, k, v = W.qkv(n, hq, hkv, dh, 1.0 / dh, dtype, 21)
+    pos = torch.from_numpy(np.sort(np.random.default_rng(n).choice(max_pos, n, replace=False)).astype(np.int32))
+    pos[0] = 0
+    pos[-1] = max_pos - 1
+    table = gpu_lib.tg_rope_table(max_pos, dh, base, DEV)
+    qd = q.to(DEV)
+    _, kc, vc = gpu_lib.tg_rope_kv(qd, k.to(DEV), v.to(DEV), pos.to(DEV), table)
+    torch.cuda.synchronize()
+    wq = ref_rope(q, pos.numpy(), base)
+    wk = ref_rope(k, pos.numpy(), base)
+    tol = 2.0 ** -8 if dtype == torch.bfloat16 else 1e-6
+    for got, want in ((qd, wq), (kc, wk)):
+        got = got.cpu().double().numpy()
+        assert np.all(np.abs(got - want) <= tol * np.abs(want) + 1e-6), float(np.max(np.abs(got - want)))
+    assert torch.equal(vc.cpu(), v)
+
+
+def test_rope_table_matches_fp64_angles(gpu_lib):
+    dh, base, max_pos = 128, 1e6, 131072
+    t = gpu_lib.tg_rope_table(max_pos, dh, base, DEV).cpu().double().numpy()
+    rows = np.array([0, 1, 2, 1000, 65535, 131071])
+    theta = np.power(base, -2.0 * np.arange(dh // 2) / dh)
+    phi = rows[:, None] * theta[None, :]
+    want = np.concatenate([np.cos(phi), np.sin(phi)], axis=1).astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(t[rows] - want)) <= 1.2e-7
+
+
+# ----------------------------------------------------------------------------- attention
+def _attn_inputs(n, hq, hkv, dh, dtype, seed, gkind="uniform", pos_kind="sparse"):
+    q, k, v = W.qkv(n, hq, hkv, dh, 1.0 / dh, dtype, seed)
+    if gkind == "uniform":
+        g = W.random_scores(n, seed)
+    elif gkind == "wide":
+        g = W.gate_values_wide(n, seed)
+    elif gkind == "edge":
+        g = W.random_scores(n, seed)
+        g[::5] = 0.0
+        g[1::5] = 1.0
+        g[2::7] = 1e-30
+    else:
+        raise ValueError(gkind)
+    if pos_kind == "sparse":
+        pos = np.sort(np.random.default_rng(seed).choice(max(4 * n, 1), n, replace=False)).astype(np.int32)
+    else:
+        pos = np.arange(n, dtype=np.int32)
+    return q, k, v, g, torch.from_numpy(pos)
+
+
+def _run_attn(tg, q, k, v, g, pos):
+    o, lse = tg.tg_gated_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV), want_lse=True)
+    torch.cuda.synchronize()
+    return o.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def test_attn_tiny_fp32(gpu_lib):
+    sh = W.SHAPES["tiny"]
+    _say("attn tiny fp32")
+    q, k, v, g, pos = _attn_inputs(sh.k, sh.hq, sh.hkv, sh.dh, torch.float32, W.SEEDS["tiny"])
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy())
+    assert np.max(np.abs(o - wo)) <= 1e-4
+    assert np.max(np.abs(lse - wl)) <= 1e-4
+
+
+@pytest.mark.parametrize("n,hq,hkv,dh,gkind", [(300, 4, 2, 64, "uniform"), (300, 16, 8, 128, "wide"),
+                                               (1, 4, 4, 128, "uniform"), (63, 8, 1, 128, "edge"),
+                                               (129, 2, 2, 64, "edge"), (640, 6, 3, 128, "uniform"),
+                                               (257, 16, 8, 128, "uniform")])
+def test_attn_bf16_shapes(gpu_lib, n, hq, hkv, dh, gkind):
+    _say("attn bf16", n, hq, hkv, dh, gkind)
+    q, k, v, g, pos = _attn_inputs(n, hq, hkv, dh, torch.bfloat16, n + hq, gkind)
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy())
+    err = float(np.max(np.abs(o - wo)))
+    _say("  max abs err o", err, "lse", float(np.max(np.abs(lse - wl))))
+    assert err <= 2e-2
+    assert np.max(np.abs(lse - wl)) <= 1e-3
+
+
+@pytest.mark.parametrize("n,hq,hkv,dh", [(200, 4, 2, 64), (77, 2, 1, 128)])
+def test_attn_fp32_shapes(gpu_lib, n, hq, hkv, dh):
+    q, k, v, g, pos = _attn_inputs(n, hq, hkv, dh, torch.float32, n, "edge")
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy())
+    assert np.max(np.abs(o - wo)) <= 1e-4
+    assert np.max(np.abs(lse - wl)) <= 1e-4
+
+
+def _sample_rows(n, seed, count=192):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1]
+    rows = np.unique(np.concatenate([[r for r in fixed if 0 <= r < n], rng.choice(n, count, replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("name,gkind", [("qwen1p7b_32k", "uniform"), ("qwen1p7b_128k", "wide")])
+def test_attn_bf16_full_size_sampled_rows(gpu_lib, name, gkind):
+    sh = W.SHAPES[name]
+    _say("attn full size", name, sh.k)
+    q, k, v, g, pos = _attn_inputs(sh.k, sh.hq, sh.hkv, sh.dh, torch.bfloat16, W.SEEDS[name], gkind)
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    rows = _sample_rows(sh.k, 5)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy(), rows=rows)
+    err = float(np.max(np.abs(o[rows] - wo)))
+    _say("  max abs err o", err)
+    assert err <= 2e-2
+    assert np.max(np.abs(lse[:, rows] - wl)) <= 1e-3
+    assert np.all(np.isfinite(o))
+
+
+def test_attn_varlen_ragged(gpu_lib):
+    lens = [256, 1, 100, 256, 129, 0, 256]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    q, k, v = W.qkv(total, 16, 8, 128, 1.0 / 128, torch.bfloat16, 31)
+    g = W.random_scores(total, 31)
+    pos = np.concatenate([np.sort(np.random.default_rng(b).choice(40000, n, replace=False)) for b, n in
+                          enumerate(lens)]).astype(np.int32)
+    o, lse = gpu_lib.tg_gated_attn_varlen(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV),
+                                          torch.from_numpy(pos).to(DEV), torch.from_numpy(cu).to(DEV),
+                                          max(lens), want_lse=True)
+    torch.cuda.synchronize()
+    wo, wl = ref_attn_varlen(q, k, v, g, pos, cu)
+    assert np.max(np.abs(o.cpu().double().numpy() - wo)) <= 2e-2
+    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= 1e-3
+
+
+def test_attn_first_query_is_its_own_value(gpu_lib):
+    q, k, v, g, pos = _attn_inputs(200, 4, 2, 128, torch.bfloat16, 3)
+    o, _ = _run_attn(gpu_lib, q, k, v, g, pos)
+    np.testing.assert_array_equal(o[0], v[0, [0, 0, 1, 1]].double().numpy())
+
+
+# ----------------------------------------------------------------------------- end to end
+def test_end_to_end_qwen_32k(gpu_lib):
+    """The full path at the 32k workload: each stage checked against the oracle
+    with that stage's input taken from the previous GPU stage (shared bytes)."""
+    tg = gpu_lib
+    sh = W.SHAPES["qwen1p7b_32k"]
+    seed = W.SEEDS["qwen1p7b_32k"]
+    _say("end-to-end 32k")
+    h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac)
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+    hd = h.to(DEV)
+    g = tg.tg_gate_score(hd, w1.to(DEV), b1.to(DEV), w2.to(DEV), b2)
+    idx = tg.tg_select_topk(g, sh.k, sh.q_len)
+    hk, gk, pos = tg.tg_gather(hd, g, idx)
+    q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed)
+    table = tg.tg_rope_table(sh.n, sh.dh, sh.rope_base, DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    _, kc, vc = tg.tg_rope_kv(qd, kd, vd, pos, table)
+    o, lse = tg.tg_gated_attn(qd, kc, vc, gk, pos, want_lse=True)
+    torch.cuda.synchronize()
+
+    g_ref, _ = ref_gate(h, w1, b1, w2, b2)
+    assert _rel_err(g.cpu().numpy(), g_ref) <= 1e-2
+    g_cpu = g.cpu().numpy()
+    idx_ref = ref_select(g_cpu, sh.k, sh.q_len)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    overlap = len(np.intersect1d(idx_ref, ref_select(g_ref.astype(np.float32), sh.k, sh.q_len))) / sh.k
+    _say("  kept-set overlap with the oracle's own gate values:", overlap)
+    wh, wg, wp = ref_gather(h.view(torch.int16).numpy(), g_cpu, idx_ref)
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16).numpy(), wh)
+    np.testing.assert_array_equal(gk.cpu().numpy(), wg)
+    np.testing.assert_array_equal(pos.cpu().numpy(), wp)
+    assert np.all(np.abs(qd.cpu().double().numpy() - ref_rope(q, wp, sh.rope_base)) <=
+                  2.0 ** -8 * np.abs(ref_rope(q, wp, sh.rope_base)) + 1e-6)
+    rows = _sample_rows(sh.k, 8)
+    wo, wl = ref_attn(qd.cpu(), kc.cpu(), vc.cpu(), wg, wp, rows=rows)
+    assert np.max(np.abs(o.cpu().double().numpy()[rows] - wo)) <= 2e-2
+    assert np.max(np.abs(lse.cpu().double().numpy()[:, rows] - wl)) <= 1e-3
+
+
+def test_repeat_runs_are_bitwise_identical(gpu_lib):
+    tg = gpu_lib
+    g = W.random_scores(32768, 2).to(DEV)
+    q, k, v, gk, pos = _attn_inputs(1000, 16, 8, 128, torch.bfloat16, 4)
+    q, k, v, gk, pos = (t.to(DEV) for t in (q, k, v, gk, pos))
+    first = None
+    for _ in range(5):
+        idx = tg.tg_select_topk(g, 4096, 64)
+        o = tg.tg_gated_attn(q, k, v, gk, pos)
+        torch.cuda.synchronize()
+        cur = (idx.cpu(), o.cpu())
+        if first is None:
+            first = cur
+        else:
+            assert torch.equal(cur[0], first[0]) and torch.equal(cur[1].view(torch.int16), first[1].view(torch.int16))
