@@ -1,0 +1,331 @@
+"""Benchmark of the TokenGate gated-prefill hot path on one MI355X.
+
+A step is one pass of the whole path over one prompt of the workload:
+gate MLP over all N tokens -> top-K select (question tail kept) -> gather of
+the kept rows, gate values and positions -> for each upper layer: RoPE + the
+compact KV cache, then token-gated causal GQA attention.  Inputs are resident
+in HBM before timing starts; three copies of the hidden states rotate between
+steps so that the 256 MB last-level cache cannot serve the gate's input.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen1p7b_32k]
+
+Prints one JSON line.  `value` is tokens/s (prompt tokens N per step time).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill tokens/s (gate+topK+gated attn) @N=32k,K=4k; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ATTN_KERNEL_SOURCE = os.path.join(ROOT, "learned_token_pruning_03_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_qwen1p7b_32k_traffic.json")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen1p7b_32k", choices=["qwen1p7b_32k", "qwen1p7b_128k", "stack19"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
+    return p.parse_args(argv)
+
+
+def _file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Path:
+    """Device buffers and the launch sequence of one workload."""
+
+    def __init__(self, tg, W, name, dev):
+        import torch
+        sh = W.SHAPES[name]
+        seed = W.SEEDS[name]
+        self.tg, self.sh, self.dev = tg, sh, dev
+        copies = 3
+        self.h = [W.hidden_states(sh.n, sh.d, sh.dtype, seed + 100 * c, planted_frac=sh.planted_frac).to(dev)
+                  for c in range(copies)]
+        w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+        self.w1, self.b1, self.w2, self.b2 = w1.to(dev), b1.to(dev), w2.to(dev), b2
+        self.layers = []
+        for layer in range(sh.layers):
+            q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed * 1000 + layer)
+            self.layers.append((q.to(dev), k.to(dev), v.to(dev), torch.empty_like(k, device=dev),
+                                torch.empty_like(v, device=dev), torch.empty_like(q, device=dev)))
+        self.table = tg.tg_rope_table(sh.n, sh.dh, sh.rope_base, dev)
+        kept = min(sh.k, sh.n)
+        f32, i32 = torch.float32, torch.int32
+        self.g = torch.empty(sh.n, dtype=f32, device=dev)
+        self.idx = torch.empty(kept, dtype=i32, device=dev)
+        self.hk = torch.empty(kept, sh.d, dtype=sh.dtype, device=dev)
+        self.gk = torch.empty(kept, dtype=f32, device=dev)
+        self.pos = torch.empty(kept, dtype=i32, device=dev)
+        self.lse = torch.empty(sh.hq, kept, dtype=f32, device=dev)
+        self.wide_g = None
+        if name == "qwen1p7b_128k":  # select/attention use a widely spread gate vector
+            self.wide_g = W.gate_values_wide(sh.n, seed).to(dev)
+        self.step_no = 0
+
+    # The five stages, each a single library call.
+    def gate(self):
+        tg = self.tg
+        h = self.h[self.step_no % len(self.h)]
+        tg.tg_gate_score(h, self.w1, self.b1, self.w2, self.b2, g=self.g)
+
+    def select(self):
+        g = self.g if self.wide_g is None else self.wide_g
+        self.tg.tg_select_topk(g, self.sh.k, self.sh.q_len, idx=self.idx)
+
+    def gather(self):
+        g = self.g if self.wide_g is None else self.wide_g
+        h = self.h[self.step_no % len(self.h)]
+        self.tg.tg_gather(h, g, self.idx, h_out=self.hk, g_out=self.gk, pos_out=self.pos)
+
+    def rope(self, layer):
+        q, k, v, kc, vc, _ = self.layers[layer]
+        self.tg.tg_rope_kv(q, k, v, self.pos, self.table, k_cache=kc, v_cache=vc)
+
+    def attn(self, layer):
+        q, _, _, kc, vc, o = self.layers[layer]
+        self.tg.tg_gated_attn(q, kc, vc, self.gk, self.pos, o=o, lse=self.lse)
+
+    def step(self):
+        self.gate()
+        self.select()
+        self.gather()
+        for layer in range(self.sh.layers):
+            self.rope(layer)
+            self.attn(layer)
+        self.step_no += 1
+
+
+def attn_flops(sh):
+    """Algorithmic flops of one causal attention launch: 2 products (QK^T and
+    PV) x 2 flop per multiply-add x Dh x Hq x visible (query, key) pairs."""
+    k = min(sh.k, sh.n)
+    return 4.0 * sh.dh * sh.hq * k * (k + 1) / 2.0
+
+
+def gate_flops(sh):
+    return 2.0 * sh.n * sh.d * sh.hidden + 4.0 * sh.n * sh.hidden
+
+
+def stage_bytes(sh):
+    k = min(sh.k, sh.n)
+    es = 2
+    return {
+        "gate": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4,
+        "select": sh.n * 4 + k * 4,
+        "gather": 2 * k * (sh.d * es + 8),
+        "rope_kv": k * (2 * (sh.hq + sh.hkv) * sh.dh * es + 2 * sh.hkv * sh.dh * es + sh.dh * 4),
+        "attn": k * (sh.hq * sh.dh * es * 2 + 2 * sh.hkv * sh.dh * es + 8),
+    }
+
+
+def time_stages(path, reps):
+    import torch
+    sh = path.sh
+    names = ["gate", "select", "gather", "rope_kv", "attn"]
+    samples = {n: [] for n in names}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+    for _ in range(reps):
+        ev[0].record()
+        path.gate()
+        ev[1].record()
+        ev[2].record()
+        path.select()
+        ev[3].record()
+        ev[4].record()
+        path.gather()
+        ev[5].record()
+        ev[6].record()
+        path.rope(0)
+        ev[7].record()
+        ev[8].record()
+        path.attn(0)
+        ev[9].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            samples[n].append(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3)  # us
+        path.step_no += 1
+    return {n: statistics.median(v) for n, v in samples.items()}, {n: sum(v) / len(v) for n, v in samples.items()}
+
+
+def cpu_baseline(W, name):
+    """The oracle, untouched, on a bounded sample of the same workload, scaled
+    to the whole prompt: half of the gate rows, the full select and gather, the
+    full RoPE, and 512 random query rows of the attention (scaled by the exact
+    count of visible query-key pairs)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    sh = W.SHAPES[name]
+    seed = W.SEEDS[name]
+    h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac)
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+    q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed * 1000)
+    rows_gate = sh.n // 2
+    t0 = time.perf_counter()
+    g, _ = O.ref_gate(h[:rows_gate], w1, b1, w2, b2)
+    t_gate = (time.perf_counter() - t0) * sh.n / rows_gate
+    g_full = np.concatenate([g, g])[: sh.n].astype(np.float32)
+    t0 = time.perf_counter()
+    idx = O.ref_select(g_full, sh.k, sh.q_len)
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hk, gk, pos = O.ref_gather(h.view(torch.int16).numpy(), g_full, idx)
+    t_gat = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.ref_rope_kv(q, k, v, pos, sh.rope_base)
+    t_rope = time.perf_counter() - t0
+    kk = len(idx)
+    rows = np.sort(np.random.default_rng(seed).choice(kk, 512, replace=False))
+    t0 = time.perf_counter()
+    O.ref_attn(q, k, v, gk, pos, rows=rows)
+    t_attn = (time.perf_counter() - t0) * (kk * (kk + 1) / 2) / float(np.sum(rows + 1))
+    total = t_gate + t_sel + t_gat + sh.layers * (t_rope + t_attn)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": sh.n / total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle on the same seeded {name} inputs: gate on {rows_gate} of {sh.n} rows, "
+                   f"full select/gather/RoPE, attention on 512 of {kk} query rows (all heads); each stage "
+                   f"scaled to the full prompt"),
+        "stage_s": {"gate": t_gate, "select": t_sel, "gather": t_gat, "rope_kv": t_rope, "attn": t_attn},
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def load_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary,
+    valid only while the attention kernel source is the one it was taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != _file_sha(ATTN_KERNEL_SOURCE):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        return 2
+    import torch
+
+    import learned_token_pruning_03_amd as tg
+    import learned_token_pruning_03_amd.workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    tg.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    path = Path(tg, W, args.workload, dev)
+    sh = path.sh
+    print(f"[bench] workload {args.workload}: N={sh.n} K={sh.k} layers={sh.layers}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        path.step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    tokens_per_s = sh.n * args.steps / (ms_total / 1e3)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    med, mean = time_stages(path, args.stage_reps)
+    print(f"[bench] stage medians (us): {json.dumps({k: round(v, 2) for k, v in med.items()})}",
+          file=sys.stderr, flush=True)
+    fl_attn = attn_flops(sh)
+    fl_gate = gate_flops(sh)
+    by = stage_bytes(sh)
+    attn_tflops = fl_attn / (mean["attn"] * 1e-6) / 1e12
+    traffic = load_traffic()
+    roofline = {
+        "kernel": "attn_bf16_kernel<128>",
+        "bound": "mfma",
+        "achieved": round(attn_tflops, 1),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "flops_per_launch": fl_attn,
+        "avg_launch_us": round(mean["attn"], 2),
+    }
+    stages = {}
+    for n in ["gate", "select", "gather", "rope_kv", "attn"]:
+        e = {"median_us": round(med[n], 2), "mean_us": round(mean[n], 2),
+             "GB/s": round(by[n] / (med[n] * 1e-6) / 1e9, 1)}
+        if n == "gate":
+            e["TFLOP/s"] = round(fl_gate / (med[n] * 1e-6) / 1e12, 1)
+        if n == "attn":
+            e["TFLOP/s"] = round(fl_attn / (med[n] * 1e-6) / 1e12, 1)
+        stages[n] = e
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(W, args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": sh.n, "k": sh.k, "q_len": sh.q_len, "d": sh.d,
+                   "gate_hidden": sh.hidden, "hq": sh.hq, "hkv": sh.hkv, "dh": sh.dh,
+                   "upper_layers": sh.layers, "global_batch": 1, "seq_len": sh.n},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "gate_pct_hbm_peak": round(100 * by["gate"] / (med["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        "gather_pct_hbm_peak": round(100 * by["gather"] / (med["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
