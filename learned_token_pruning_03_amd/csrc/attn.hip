@@ -5,11 +5,12 @@
 // renormalised); the page's Abstract and the aitualizate.com article, section
 // "Cómo consigue entrenar una selección top-K": the importance score is a
 // bias on the attention logits.  Both give softmax_j(scale*q.k_j + ln g_j).
-// In base 2:  t_ij = (scale*log2 e) * q_i.k_j + log2 max(g_j, FLT_MIN),
-// p_ij = 2^(t_ij - m_i), which is one FMA per logit; the bias enters the
-// running maximum and the running sum like any other part of the logit.
+// In base 2 with c = scale*log2 e:  t_ij = c * (q_i.k_j + log2 max(g_j, FLT_MIN) / c),
+// p_ij = 2^(t_ij - m_i).  The bias term, divided by c, seeds the QK^T
+// accumulator, so it enters the logit inside the MFMA and then takes part in
+// the running maximum and the running sum like any other part of the logit.
 //
-// bf16 kernel layout (one workgroup = 512 threads = 8 waves):
+// bf16 kernel (one workgroup = 512 threads = 8 waves, two per SIMD):
 //  * a workgroup owns one query head and a pair of 128-query tiles, tile
 //    (T-1-p) then tile p, so that every workgroup has the same causal work;
 //  * the two 4-wave groups split each tile's key range (group 0 takes the
@@ -17,14 +18,19 @@
 //    (max, sum, output) through LDS at the end of the tile;
 //  * inside a group each wave owns 32 queries.  S^T = K Q^T runs on
 //    v_mfma_f32_32x32x16_bf16 with Q held in registers as the B operand, so
-//    each lane ends up owning one query: the row max, row sum and rescale
-//    are per-lane scalars, and P^T leaves the accumulators directly as the B
+//    each lane owns one query: its row max, row sum and rescale factor are
+//    per-lane scalars, and P^T leaves the accumulators directly as the B
 //    operand of O^T = V^T P^T (no LDS round trip for P);
-//  * K is staged row-major and V transposed in LDS (padded rows, no bank
-//    conflicts for the fragment reads), double-buffered, the next tile
-//    prefetched into registers during the current tile's MFMAs;
-//  * blockIdx -> (KV head, query head) is arranged so that all query heads
-//    of one KV head land on the same XCD and share its L2.
+//  * K and V tiles go from global memory straight into LDS (global_load_lds,
+//    XOR-swizzled 256-byte rows, double-buffered per group, the two stages in
+//    separate LDS objects so that reads of one stage never wait for the
+//    loads into the other); the V^T operand is read with ds_read_b64_tr_b16,
+//    the transposing LDS read, so V needs no transposition pass;
+//  * the causal test runs only on tiles reaching past a wave's first query,
+//    comparing original positions; earlier keys are visible because positions
+//    increase with the kept index;
+//  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
+//    the same XCD, where they share that head's K/V in L2.
 #include <cmath>
 
 #include "tg_internal.h"
@@ -52,30 +58,37 @@ struct AttnCfg {
   static constexpr int BM = 128;                 // queries per tile (4 waves x 32)
   static constexpr int BN = 64;                  // keys per tile
   static constexpr int CPR = DH / 8;             // 16-byte chunks per K/V row
-  static constexpr int KROW = DH * 2 + 16;       // padded LDS bytes per K row
-  static constexpr int VROW = BN * 2 + 8;        // padded LDS bytes per V^T row
-  static constexpr int K_BYTES = BN * KROW;
-  static constexpr int V_BYTES = DH * VROW;
+  static constexpr int ROW = DH * 2;             // LDS bytes per K or V row (XOR-swizzled chunks)
+  static constexpr int K_BYTES = BN * ROW;
+  static constexpr int V_BYTES = BN * ROW;
   static constexpr int STAGE = K_BYTES + V_BYTES + BN * 8;  // + bias f32 + pos i32
-  static constexpr int GROUP_BYTES = 2 * STAGE;
-  static constexpr int LDS_BYTES = 2 * GROUP_BYTES;
-  static constexpr int KL = BN * CPR / 256;      // K chunks per group thread
-  static constexpr int VP = CPR / 8;             // V chunk columns per thread (x2 keys)
+  static constexpr int STAGE_BYTES = 2 * STAGE;  // both groups' copy of one pipeline stage
+  static constexpr int DMA = BN * CPR / 256;     // 16-byte direct loads per thread per tensor
   static constexpr int MD = DH / 32;             // 32-row blocks of O^T
-  static_assert(4 * 64 * (DH / 2 + 2) * 4 <= LDS_BYTES, "merge scratch must fit");
+  static_assert(4 * 64 * (DH / 2) * 4 <= STAGE_BYTES, "merge scratch (O) must fit in one stage array");
+  // Chunk c of row r is stored at chunk c ^ swz(r).  K rows are read by
+  // ds_read_b128 (16 consecutive rows, one chunk), V rows by the transposing
+  // read (4 consecutive rows x 4 consecutive chunks per half-wave).
+  static __device__ __forceinline__ int swz_k(int r) { return DH == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int DH>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   using C = AttnCfg<DH>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+  // The two pipeline stages are separate LDS objects, so the compiler can
+  // tell that reads of one stage never alias the direct loads into the other
+  // and does not make them wait for those loads.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform indices live in scalar registers (readfirstlane), so branches
+  // on them are scalar branches rather than exec-masked regions.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int w4 = wave & 3;
   const int gtid = tid & 255;
@@ -99,38 +112,45 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const uint8_t* kbase = a.k + ((s0 * hkv + kvh) * DH) * 2;
   const uint8_t* vbase = a.v + ((s0 * hkv + kvh) * DH) * 2;
   const int64_t kv_stride = (int64_t)hkv * DH * 2;  // bytes between consecutive keys
-  uint8_t* gbase = lds + grp * C::GROUP_BYTES;
+  uint8_t* gbase_a = lds_a + grp * C::STAGE;
+  uint8_t* gbase_b = lds_b + grp * C::STAGE;
 
-  // Prefetch registers for one K/V tile (per group thread).
-  u32x4 kreg[C::KL];
-  u32x4 vreg[2 * C::VP];
+  // Gate bias and position of one key per thread (threads < 64 of a group),
+  // staged in registers; K and V go straight from global memory to LDS.
   float breg = 0.0f;
   int preg = 0;
-
-  auto load_tile = [&](int kt) {
+  const int64_t tile_stride = (int64_t)C::BN * kv_stride;
+  const float inv_c = 1.0f / a.scale_log2;
+  // Direct load i of this thread fills LDS chunk P = i*256 + gtid of the tile:
+  // row P / CPR, stored position P % CPR, holding logical chunk pos ^ swz(row).
+  uint32_t dma_k[C::DMA], dma_v[C::DMA];
+  int dma_row[C::DMA];
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int key = gtid / C::CPR + i * (256 / C::CPR);
-      const int c = gtid % C::CPR;
-      int j = kt * C::BN + key;
-      j = j < L ? j : L - 1;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + j * kv_stride + c * 16);
-    }
+  for (int i = 0; i < C::DMA; ++i) {
+    const int P = i * 256 + gtid;
+    const int r = P / C::CPR, pos = P % C::CPR;
+    dma_row[i] = r;
+    dma_k[i] = (uint32_t)((pos ^ C::swz_k(r)) * 16);
+    dma_v[i] = (uint32_t)((pos ^ C::swz_v(r)) * 16);
+  }
+  const int wave_in_group = w4;
+  auto issue_tile = [&](int kt, uint8_t* sb) __attribute__((always_inline)) {
+    const bool full = (kt + 1) * C::BN <= L;
 #pragma unroll
-    for (int i = 0; i < C::VP; ++i) {
-      const int kp = gtid & 31;
-      const int c = (gtid >> 5) + 8 * i;
-      int j0 = kt * C::BN + 2 * kp;
-      int j1 = j0 + 1;
-      j0 = j0 < L ? j0 : L - 1;
-      j1 = j1 < L ? j1 : L - 1;
-      vreg[2 * i] = *reinterpret_cast<const u32x4*>(vbase + j0 * kv_stride + c * 16);
-      vreg[2 * i + 1] = *reinterpret_cast<const u32x4*>(vbase + j1 * kv_stride + c * 16);
+    for (int i = 0; i < C::DMA; ++i) {
+      const int j = full ? kt * C::BN + dma_row[i] : min(kt * C::BN + dma_row[i], L - 1);
+      const uint8_t* krow = kbase + (uint32_t)j * (uint32_t)kv_stride;
+      const uint8_t* vrow = vbase + (uint32_t)j * (uint32_t)kv_stride;
+      uint8_t* dst = sb + (i * 256 + wave_in_group * 64) * 16;  // wave-uniform; lane l lands at +16 l
+      __builtin_amdgcn_global_load_lds((const void*)(krow + dma_k[i]),
+                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vrow + dma_v[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + C::K_BYTES), 16, 0, 0);
     }
     if (gtid < C::BN) {
       const int j = kt * C::BN + gtid;
       if (j < L) {
-        breg = log2f(fmaxf(a.g[s0 + j], kFltMin));
+        breg = a.g[s0 + j];
         preg = a.pos[s0 + j];
       } else {
         breg = -INFINITY;
@@ -138,31 +158,31 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    uint8_t* sb = gbase + stage * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int key = gtid / C::CPR + i * (256 / C::CPR);
-      const int c = gtid % C::CPR;
-      *reinterpret_cast<u32x4*>(sb + key * C::KROW + c * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VP; ++i) {
-      const int kp = gtid & 31;
-      const int c = (gtid >> 5) + 8 * i;
-      uint8_t* vt = sb + C::K_BYTES + (8 * c) * C::VROW + kp * 4;
-      const u32x4 x0 = vreg[2 * i], x1 = vreg[2 * i + 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t*>(vt + (2 * e) * C::VROW) = lo16x2(x0[e], x1[e]);
-        *reinterpret_cast<uint32_t*>(vt + (2 * e + 1) * C::VROW) = hi16x2(x0[e], x1[e]);
-      }
-    }
+  // Completes a tile issued by issue_tile: bias and positions into LDS after
+  // every outstanding global load (the direct K/V loads included) has landed.
+  auto finish_tile = [&](uint8_t* sb) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0)
     if (gtid < C::BN) {
-      reinterpret_cast<float*>(sb + C::K_BYTES + C::V_BYTES)[gtid] = breg;
+      // Gate bias in units of the raw score: log2(g) / (scale*log2 e), so that
+      // it can seed the S^T accumulator and enter the logit inside the MFMA.
+      reinterpret_cast<float*>(sb + C::K_BYTES + C::V_BYTES)[gtid] =
+          (breg == -INFINITY) ? -INFINITY : log2f(fmaxf(breg, kFltMin)) * inv_c;
       reinterpret_cast<int*>(sb + C::K_BYTES + C::V_BYTES + C::BN * 4)[gtid] = preg;
     }
   };
+  // K fragment offsets (per k-step) and V^T transposing-read offsets (per
+  // 32-row block of d), including the swizzles.
+  uint32_t koff[DH / 16];
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) koff[ks] = r32 * C::ROW + (((2 * ks + half) ^ C::swz_k(r32)) * 16);
+  const int G = lane >> 4, ia = (lane >> 2) & 3, ib = lane & 3;
+  uint32_t voff[C::MD];
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    const int vrow = 4 * (G >> 1) + ia;             // + 16 kb + 8 rr (multiples of 8 keep the swizzle)
+    const int chunk = 4 * md + 2 * (G & 1) + (ib >> 1);
+    voff[md] = C::K_BYTES + vrow * C::ROW + ((chunk ^ C::swz_v(vrow)) * 16) + (ib & 1) * 8;
+  }
 
   for (int which = 0; which < 2; ++which) {
     const int mt = which == 0 ? ntiles - 1 - pair : pair;
@@ -177,6 +197,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < DH / 16; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (ks * 16 + half * 8) * 2);
     const int pos_i = a.pos[s0 + qrow];
+    // Q fragments must have landed before the loop: otherwise the wait-count
+    // bookkeeping at the loop header merges them with the in-flight prefetch
+    // and every QK^T MFMA waits on the next tile's global loads.
+    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0): gfx9 encoding, lgkm/exp counts untouched
 
     const int kend = min(L, row0 + C::BM);
     const int n_kt = (kend + C::BN - 1) / C::BN;
@@ -191,95 +215,108 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
 
     if (grp < n_kt) {
-      load_tile(grp);
-      store_tile(0);
+      issue_tile(grp, gbase_a);
+      finish_tile(gbase_a);
     }
     __syncthreads();
 
-    for (int it = 0; it < niter; ++it) {
+    auto step = [&](int it, uint8_t* cur, uint8_t* nb) __attribute__((always_inline)) {
       const int kt = 2 * it + grp;
       const int nxt = kt + 2;
-      if (nxt < n_kt) load_tile(nxt);
+      if (nxt < n_kt) issue_tile(nxt, nb);
       if (kt < n_kt) {
-        const uint8_t* sb = gbase + (it & 1) * C::STAGE;
-        // ---- S^T = K Q^T for 64 keys x this wave's 32 queries ----
+        const uint8_t* sb = cur;
+        // ---- S^T = bias + K Q^T for 64 keys x this wave's 32 queries ----
+        const float* bias = reinterpret_cast<const float*>(sb + C::K_BYTES + C::V_BYTES);
         f32x16 sacc[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.0f;
+          for (int rq = 0; rq < 4; ++rq) {
+            const f32x4 bj = *reinterpret_cast<const f32x4*>(bias + mb * 32 + 8 * rq + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[mb][4 * rq + e] = bj[e];
+          }
 #pragma unroll
         for (int ks = 0; ks < DH / 16; ++ks) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + (mb * 32 + r32) * C::KROW +
-                                                               (ks * 16 + half * 8) * 2);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + mb * 32 * C::ROW + koff[ks]);
             sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
           }
         }
-        // ---- gated logits, online softmax (base 2) ----
-        const float* bias = reinterpret_cast<const float*>(sb + C::K_BYTES + C::V_BYTES);
+        // ---- online softmax (base 2); logits t = c * S^T ----
         const int* kpos = reinterpret_cast<const int*>(sb + C::K_BYTES + C::V_BYTES + C::BN * 4);
-        const bool masked_tile = kt * C::BN + C::BN - 1 > row0 + w4 * 32;
-        float mloc = -INFINITY;
+        // Causal test only on tiles reaching past this wave's first query.
+        if (kt * C::BN + C::BN - 1 > row0 + w4 * 32) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int j0 = mb * 32 + 8 * rq + 4 * half;  // 4 consecutive keys
-            const f32x4 bj = *reinterpret_cast<const f32x4*>(bias + j0);
+            for (int rq = 0; rq < 4; ++rq) {
+              const u32x4 pj = *reinterpret_cast<const u32x4*>(kpos + mb * 32 + 8 * rq + 4 * half);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float x = fmaf(sacc[mb][4 * rq + e], a.scale_log2, bj[e]);
-              if (masked_tile && kpos[j0 + e] > pos_i) x = -INFINITY;
-              sacc[mb][4 * rq + e] = x;
-              mloc = fmaxf(mloc, x);
+              for (int e = 0; e < 4; ++e)
+                sacc[mb][4 * rq + e] = ((int)pj[e] > pos_i) ? -INFINITY : sacc[mb][4 * rq + e];
             }
-          }
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const float m_new = fmaxf(m, mloc);
-        const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - msub);
-        float psum = 0.0f;
+        float mloc = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sacc[mb][r] - msub);
-            sacc[mb][r] = p;
+          for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mb][r]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_new = fmaxf(m, mloc * a.scale_log2);
+        const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+        float psum = 0.0f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + e], a.scale_log2, -msub));
             psum += p;
+            pf[kb][e] = (__bf16)p;
           }
-        lsum = fmaf(lsum, alpha, psum);
-        m = m_new;
+        // Rescale only when some lane's running maximum moved (else the factor is exactly 1).
+        if (__any(m_new > m)) {
+          const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - msub);
+          lsum *= alpha;
 #pragma unroll
-        for (int md = 0; md < C::MD; ++md)
+          for (int md = 0; md < C::MD; ++md)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+            for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+          m = m_new;
+        }
+        lsum += psum;
         // ---- O^T += V^T P^T ----
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          bf16x8 pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kb >> 1][8 * (kb & 1) + e];
 #pragma unroll
           for (int md = 0; md < C::MD; ++md) {
-            const uint8_t* vrow = sb + C::K_BYTES + (md * 32 + r32) * C::VROW;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (kb * 16 + 4 * half) * 2);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (kb * 16 + 8 + 4 * half) * 2);
-            const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf,
-                                                              oacc[md], 0, 0, 0);
+            const uint8_t* vp = sb + voff[md] + (16 * kb) * C::ROW;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * C::ROW));
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb], oacc[md], 0, 0, 0);
           }
         }
       }
-      if (nxt < n_kt) store_tile((it + 1) & 1);
+      if (nxt < n_kt) finish_tile(nb);
       __syncthreads();
+    };
+    for (int it = 0; it < niter; it += 2) {
+      step(it, gbase_a, gbase_b);
+      if (it + 1 < niter) step(it + 1, gbase_b, gbase_a);
     }
 
     // ---- merge the two groups' partial results, normalise, store ----
-    float* scr = reinterpret_cast<float*>(lds);
-    float* scr_m = scr + 4 * 64 * (DH / 2);
+    float* scr = reinterpret_cast<float*>(lds_a);
+    float* scr_m = reinterpret_cast<float*>(lds_b);
     float* scr_l = scr_m + 4 * 64;
     if (grp == 1) {
 #pragma unroll

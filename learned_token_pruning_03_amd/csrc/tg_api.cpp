@@ -196,13 +196,15 @@ TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t 
 }
 
 // ---------------------------------------------------------------------------
-static tg_status check_attn(tg_dtype dtype, int32_t hq, int32_t hkv, int32_t dh, float scale,
-                            const void* q, const void* k, const void* v, const float* g,
+static tg_status check_attn(tg_dtype dtype, int64_t max_rows, int32_t hq, int32_t hkv, int32_t dh,
+                            float scale, const void* q, const void* k, const void* v, const float* g,
                             const int32_t* pos, void* o) {
   if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "attn: unknown dtype %d", (int)dtype);
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
     return fail(TG_ERR_INVALID_ARG, "attn: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
   if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "attn: dh=%d must be 64 or 128", dh);
+  if (max_rows * hkv * dh * elem_size(dtype) >= (int64_t(1) << 31))
+    return fail(TG_ERR_UNSUPPORTED, "attn: one prompt's K (or V) must be below 2 GiB");
   if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "attn: scale must be > 0");
   if (!q || !k || !v || !g || !pos || !o) return fail(TG_ERR_INVALID_ARG, "attn: NULL pointer argument");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -229,7 +231,7 @@ TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32
                                hipStream_t stream) {
   if (n_kept < 0 || n_kept > kMaxI32) return fail(TG_ERR_INVALID_ARG, "attn: n_kept out of range");
   if (n_kept == 0) return ok();
-  tg_status st = check_attn(dtype, hq, hkv, dh, scale, q, k, v, g, pos, o);
+  tg_status st = check_attn(dtype, n_kept, hq, hkv, dh, scale, q, k, v, g, pos, o);
   if (st != TG_OK) return st;
   return from_hip(dispatch_attn(dtype, n_kept, nullptr, 1, n_kept, hq, hkv, dh, scale, q, k, v, g, pos,
                                 o, lse, stream),
@@ -244,7 +246,7 @@ TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
   if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32 || total < 0 || total > kMaxI32)
     return fail(TG_ERR_INVALID_ARG, "attn_varlen: batch, max_seqlen or total out of range");
   if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
-  tg_status st = check_attn(dtype, hq, hkv, dh, scale, q, k, v, g, pos, o);
+  tg_status st = check_attn(dtype, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o);
   if (st != TG_OK) return st;
   if (!cu_seqlens) return fail(TG_ERR_INVALID_ARG, "attn_varlen: NULL cu_seqlens");
   return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
