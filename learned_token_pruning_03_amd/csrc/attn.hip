@@ -119,7 +119,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   // staged in registers; K and V go straight from global memory to LDS.
   float breg = 0.0f;
   int preg = 0;
-  const int64_t tile_stride = (int64_t)C::BN * kv_stride;
   const float inv_c = 1.0f / a.scale_log2;
   // Direct load i of this thread fills LDS chunk P = i*256 + gtid of the tile:
   // row P / CPR, stored position P % CPR, holding logical chunk pos ^ swz(row).

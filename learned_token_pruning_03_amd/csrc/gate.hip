@@ -8,10 +8,15 @@
 //
 // bf16 kernel: one workgroup = 128 tokens x all `hidden` units, so the w2 dot
 // and the sigmoid finish inside the workgroup with no second pass.  The
-// h-by-W1^T product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
-// h and W1 are staged through LDS in 64-element k-chunks, double-buffered,
-// with the next chunk prefetched into registers while the current one feeds
-// the matrix cores.  The hidden layer never leaves fp32 registers.
+// h-by-W1^T product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// h and W1 stream through LDS in 64-element k-chunks over a three-stage ring
+// filled by global_load_lds (no register staging), so two chunks are always in
+// flight while the matrix cores consume the third; h is read from HBM once.
+// Eight waves, two per SIMD: waves w and w+4 own the same 64-token x H/2-unit
+// output tile and take alternate 16-wide k sub-steps, so one wave's MFMAs
+// cover the other's LDS and DMA waits.  The two partial sums meet in LDS
+// before the SiLU epilogue, which the pair also splits.  The hidden layer
+// never leaves fp32 registers.
 #include "tg_internal.h"
 
 namespace tg {
@@ -19,7 +24,7 @@ namespace {
 
 constexpr int kGateBM = 128;       // tokens per workgroup
 constexpr int kGateBK = 64;        // k elements per LDS stage (128 bytes of a row)
-constexpr int kGateThreads = 256;  // 4 waves: 2 along tokens x 2 along hidden units
+constexpr int kGateThreads = 512;  // 8 waves: 2 along tokens x 2 along hidden units x 2 along k
 
 // LDS tile rows are 128 bytes = 8 chunks of 16 bytes.  Chunk c of row r is
 // stored at chunk slot c ^ ((r >> 1) & 7): the 16 rows read by one
@@ -28,58 +33,80 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
+// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's bytes land at
+// LDS address m0 + 16 l.  Written as asm so that the compiler's wait-count
+// pass does not track it: it would otherwise drain all outstanding copies
+// before reading any stage of the ring.  The instruction has no register
+// results; completion is ordered by the explicit vmcnt waits below.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= v, nothing else.
+template <int V>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (V & 15) | ((V >> 4) << 14));
+}
+
 template <int H>
 __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int n, int d, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2, float* __restrict__ g,
     float* __restrict__ s_out) {
-  constexpr int MT = 2;               // 32-token tiles per wave
-  constexpr int NT = H / 2 / 32;      // 32-unit tiles per wave
-  constexpr int A_LOADS = kGateBM * 8 / kGateThreads;  // 16-byte chunks per thread (h)
-  constexpr int B_LOADS = H * 8 / kGateThreads;        // 16-byte chunks per thread (W1)
-  constexpr int STAGE = (kGateBM + H) * 128;           // bytes per LDS stage
+  constexpr int NW = kGateThreads / kWave;            // 8 waves
+  constexpr int MT = 2;                               // 32-token tiles per wave
+  constexpr int NT = H / 2 / 32;                      // 32-unit tiles per wave
+  constexpr int A_DMA = kGateBM * 8 / kGateThreads;   // 16-byte chunks per thread per stage (h)
+  constexpr int B_DMA = H * 8 / kGateThreads;         // same for W1
+  constexpr int PER_CHUNK = A_DMA + B_DMA;            // vmcnt increments per stage per wave
+  constexpr int H_BYTES = kGateBM * 128;
+  constexpr int STAGE = H_BYTES + H * 128;
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && (MT * NT) % 2 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
-  __shared__ float srow[2][kGateBM];
+  // Three separate objects, so the compiler can tell that reads of one stage
+  // do not depend on the DMA still landing in the other two.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
+  __shared__ float srow[4][kGateBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;   // token half
-  const int wn = wave >> 1;  // hidden-unit half
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = wave & 3;  // output tile shared by waves w and w+4
+  const int kh = wave >> 2;   // which 16-wide k sub-steps of each chunk this wave takes
+  const int wm = tile & 1;    // token half
+  const int wn = tile >> 1;   // hidden-unit half
   const int m0 = blockIdx.x * kGateBM;
 
-  // Per-thread load coordinates: chunk (16 bytes) and row within the tile.
-  const int lchunk = tid & 7;
-  const int lrow = tid >> 3;  // 0..31, +32 per load
+  // DMA mapping: instruction i of wave w fills the 1 KB block b = NW i + w of
+  // a region; lane l lands at byte 16 l of it, i.e. row 8 b + l/8, slot l%8,
+  // which holds chunk (l%8) ^ ((row >> 1) & 7).
+  const uint8_t* pa[A_DMA];
+  const uint8_t* pb[B_DMA];
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) {
+    const int r = (NW * i + wave) * 8 + (lane >> 3);
+    int row = m0 + r;
+    row = row < n ? row : n - 1;  // rows past n read a valid row, results discarded
+    pa[i] = reinterpret_cast<const uint8_t*>(h) + (int64_t)row * ld_h * 2 +
+            (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) {
+    const int r = (NW * i + wave) * 8 + (lane >> 3);
+    pb[i] = reinterpret_cast<const uint8_t*>(w1) + (int64_t)r * d * 2 +
+            (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
 
-  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
-  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w1);
-
-  u32x4 ra[A_LOADS];
-  u32x4 rb[B_LOADS];
-
-  auto load_regs = [&](int k0) {
+  auto issue = [&](int kt, uint8_t* sb) __attribute__((always_inline)) {
+    const int koff = kt * (kGateBK * 2);
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)sb;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      int row = m0 + lrow + 32 * i;
-      row = row < n ? row : n - 1;  // rows past n read a valid row, results discarded
-      ra[i] = *reinterpret_cast<const u32x4*>(hb + ((int64_t)row * ld_h + k0) * 2 + lchunk * 16);
-    }
+    for (int i = 0; i < A_DMA; ++i) dma16(pa[i] + koff, base + (NW * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int row = lrow + 32 * i;
-      rb[i] = *reinterpret_cast<const u32x4*>(wb + ((int64_t)row * d + k0) * 2 + lchunk * 16);
-    }
-  };
-  auto store_lds = [&](int stage) {
-    uint8_t* base = lds + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * i, lchunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      *reinterpret_cast<u32x4*>(base + kGateBM * 128 + swz(lrow + 32 * i, lchunk)) = rb[i];
+    for (int i = 0; i < B_DMA; ++i) dma16(pb[i] + koff, base + H_BYTES + (NW * i + wave) * 1024);
   };
 
   f32x16 acc[MT][NT];
@@ -90,58 +117,123 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = d / kGateBK;
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
-
-  const int half = lane >> 5;   // which 8-element k group of the MFMA operand
+  const int half = lane >> 5;  // which 8-element k group of the MFMA operand
   const int r32 = lane & 31;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_regs((kt + 1) * kGateBK);
-    const uint8_t* base = lds + (kt & 1) * STAGE;
+  // This wave takes sub-steps 2 kh and 2 kh + 1 of every 64-wide chunk; its
+  // partner (same tile, other kh) takes the other two.  Both fragment sets are
+  // read before the first MFMA; the second wave on the SIMD covers the wait.
+  auto compute = [&](const uint8_t* base) __attribute__((always_inline)) {
+    bf16x8 af[2][MT], bfr[2][NT];
 #pragma unroll
-    for (int ks = 0; ks < kGateBK / 16; ++ks) {
-      const int chunk = ks * 2 + half;
-      bf16x8 af[MT], bfr[NT];
+    for (int u = 0; u < 2; ++u) {
+      const int chunk = (2 * kh + u) * 2 + half;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * 64 + i * 32 + r32, chunk));
+        af[u][i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * 64 + i * 32 + r32, chunk));
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(base + kGateBM * 128 +
-                                                  swz(wn * (H / 2) + j * 32 + r32, chunk));
+        bfr[u][j] = *reinterpret_cast<const bf16x8*>(base + H_BYTES + swz(wn * (H / 2) + j * 32 + r32, chunk));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_lds((kt + 1) & 1);
-    __syncthreads();
-  }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u][i], bfr[u][j], acc[i][j], 0, 0, 0);
+  };
 
-  // Epilogue.  acc[i][j][r] holds token  wm*64 + i*32 + 8*(r/4) + 4*half + r%4
-  // and hidden unit  wn*H/2 + j*32 + r32.
+  // One ring step: chunk kt sits in stage `cur`; chunk kt+2 goes to `nxt2`,
+  // the stage every wave finished reading in the previous step.
+  auto step = [&](int kt, const int nk, uint8_t* cur, uint8_t* nxt2) __attribute__((always_inline)) {
+    if (kt + 1 < nk)
+      wait_vm<PER_CHUNK>();  // chunk kt+1 may still be landing
+    else
+      wait_vm<0>();
+    // Every wave has waited for its own share of chunk kt.  A plain barrier
+    // (no release fence) keeps chunks kt+1 and kt+2 in flight across it; the
+    // memory clobber stops the compiler moving LDS accesses over it.
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2, nxt2);
+    compute(cur);
+  };
+
+  const int nk = d / kGateBK;
+  issue(0, st0);
+  if (nk > 1) issue(1, st1);
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, nk, st0, st2);
+    step(kt + 1, nk, st1, st0);
+    step(kt + 2, nk, st2, st1);
+  }
+  if (kt < nk) step(kt, nk, st0, st2);
+  if (kt + 1 < nk) step(kt + 1, nk, st1, st0);
+
+  // ---- combine the two k halves, then the epilogue, split between partners.
+  // Of the MT*NT output tiles, tile t = i*NT + j stays with the wave whose kh
+  // equals t%2; the other half goes to the partner (wave ^ 4) through LDS.
+  // The ring is free once every wave has passed the barrier below.
+  constexpr int KEEP = MT * NT / 2;                 // tiles per wave after the split
+  constexpr int XBYTES = KEEP * 16 * kWave * 4;     // bytes one wave hands over
+  constexpr int PER_STAGE = STAGE / XBYTES;
+  static_assert(3 * PER_STAGE >= NW, "exchange fits in the ring");
+  auto region = [&](int w) __attribute__((always_inline)) {
+    const int sidx = w / PER_STAGE;
+    uint8_t* sb = sidx == 0 ? st0 : (sidx == 1 ? st1 : st2);
+    return reinterpret_cast<f32x4*>(sb + (w % PER_STAGE) * XBYTES);
+  };
+  __syncthreads();
+  {
+    f32x4* out = region(wave);
+    int q = 0;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (((i * NT + j) & 1) != kh) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            out[(q * 4 + r4) * kWave + lane] = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+          ++q;
+        }
+  }
+  __syncthreads();
+
+  // acc[i][j][r] holds token  wm*64 + i*32 + 8*(r/4) + 4*half + r%4  and
+  // hidden unit  wn*H/2 + j*32 + r32.
   float part[MT][16];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[i][r] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int unit = wn * (H / 2) + j * 32 + r32;
-    const float bias = b1 ? b1[unit] : 0.0f;
-    const float wout = w2[unit];
+  {
+    const f32x4* in = region(wave ^ 4);
+    int q = 0;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float a = acc[i][j][r] + bias;
-        const float z = a / (1.0f + expf(-a));  // SiLU
-        part[i][r] = fmaf(wout, z, part[i][r]);
-      }
+      for (int j = 0; j < NT; ++j)
+        if (((i * NT + j) & 1) == kh) {
+          const int unit = wn * (H / 2) + j * 32 + r32;
+          const float bias = b1 ? b1[unit] : 0.0f;
+          const float wout = w2[unit];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 o = in[(q * 4 + r4) * kWave + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = acc[i][j][4 * r4 + e] + o[e] + bias;
+              // SiLU(a) = a / (1 + e^-a) with the hardware exp2 and reciprocal.
+              const float ex = __builtin_amdgcn_exp2f(-a * kLog2e);
+              const float z = a * __builtin_amdgcn_rcpf(1.0f + ex);
+              part[i][4 * r4 + e] = fmaf(wout, z, part[i][4 * r4 + e]);
+            }
+          }
+          ++q;
+        }
   }
   // Sum over the 32 lanes that share a token (same `half`).
 #pragma unroll
@@ -158,13 +250,13 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        srow[wn][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = part[i][r];
+        srow[wn * 2 + kh][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = part[i][r];
   }
   __syncthreads();
   if (tid < kGateBM) {
     const int row = m0 + tid;
     if (row < n) {
-      const float sc = srow[0][tid] + srow[1][tid] + b2;
+      const float sc = (srow[0][tid] + srow[1][tid]) + (srow[2][tid] + srow[3][tid]) + b2;
       g[row] = 1.0f / (1.0f + expf(-sc));
       if (s_out) s_out[row] = sc;
     }
