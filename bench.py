@@ -41,6 +41,12 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="qwen1p7b_32k", choices=["qwen1p7b_32k", "qwen1p7b_128k", "stack19"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the run, launch a plain 1 GiB -> 1 GiB streaming kernel (torch.neg on fp32) "
+                        "three times; its PMC byte counters calibrate FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU run: reduce two rocprofv3 --pmc output folders (FETCH_SIZE, then WRITE_SIZE, "
+                        "each from a --copy-calibration run) to HBM bytes per attention launch")
     return p.parse_args(argv)
 
 
@@ -100,17 +106,21 @@ class Path:
         q, k, v, kc, vc, _ = self.layers[layer]
         self.tg.tg_rope_kv(q, k, v, self.pos, self.table, k_cache=kc, v_cache=vc)
 
-    def attn(self, layer):
+    def attn(self, layer, events=None):
         q, _, _, kc, vc, o = self.layers[layer]
+        if events is not None:  # start/end pair on the stream the kernel runs on
+            events[0].record()
         self.tg.tg_gated_attn(q, kc, vc, self.gk, self.pos, o=o, lse=self.lse)
+        if events is not None:
+            events[1].record()
 
-    def step(self):
+    def step(self, attn_events=None):
         self.gate()
         self.select()
         self.gather()
         for layer in range(self.sh.layers):
             self.rope(layer)
-            self.attn(layer)
+            self.attn(layer, None if attn_events is None else attn_events[layer])
         self.step_no += 1
 
 
@@ -228,8 +238,78 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_CAL_ELEMS = 1 << 28  # fp32 elements: 1 GiB read + 1 GiB written per launch
+
+
+def copy_calibration(torch, dev):
+    """Three launches of a plain streaming kernel of known size (torch.neg on a
+    1 GiB fp32 tensor into another): reads and writes exactly 2^30 bytes each."""
+    src = torch.ones(COPY_CAL_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _pmc_per_dispatch(folder, counter, match):
+    """Mean over dispatches of `counter` (summed over its rows) for kernels whose
+    name contains `match`, from rocprofv3 csv counter-collection output."""
+    import csv
+    import glob
+    per = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter or match not in r.get("Kernel_Name", ""):
+                    continue
+                key = (fn, r.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r} under {folder}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each
+    scaled by what the same counter reads for the 1 GiB calibration kernel."""
+    true_bytes = COPY_CAL_ELEMS * 4
+    f_attn, nf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "attn_bf16_kernel")
+    w_attn, nw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "attn_bf16_kernel")
+    f_cal, _ = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "neg")
+    w_cal, _ = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "neg")
+    f_scale = true_bytes / (f_cal * 1024.0)
+    w_scale = true_bytes / (w_cal * 1024.0)
+    fetch = f_attn * 1024.0 * f_scale
+    write = w_attn * 1024.0 * w_scale
+    from learned_token_pruning_03_amd.workloads import SHAPES
+    sh = SHAPES["qwen1p7b_32k"]
+    algo = stage_bytes(sh)["attn"]
+    rec = {
+        "kernel": "attn_bf16_kernel<128>",
+        "workload": "qwen1p7b_32k",
+        "kernel_source_sha256_16": _file_sha(ATTN_KERNEL_SOURCE),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "fetch_bytes_per_launch": round(fetch),
+        "write_bytes_per_launch": round(write),
+        "algorithmic_bytes_per_launch": algo,
+        "fetch_calibration": {"counter_kib_per_launch": f_cal, "true_bytes": true_bytes, "scale": f_scale},
+        "write_calibration": {"counter_kib_per_launch": w_cal, "true_bytes": true_bytes, "scale": w_scale},
+        "dispatches": {"fetch": nf, "write": nw},
+    }
+    return rec
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.traffic_summary:
+        rec = traffic_summary(*args.traffic_summary)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec, indent=1))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
@@ -255,13 +335,19 @@ def main(argv=None):
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # One event pair around every attention launch of the timed region: the
+    # roofline's launch duration is measured live, not in a separate loop.
+    attn_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(sh.layers)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
-        path.step()
+    for s in range(args.steps):
+        path.step(attn_ev[s])
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
+    attn_launch_us = [a.elapsed_time(b) * 1e3 for per_step in attn_ev for (a, b) in per_step]
+    attn_avg_us = sum(attn_launch_us) / len(attn_launch_us)
     ms_per_step = ms_total / args.steps
     tokens_per_s = sh.n * args.steps / (ms_total / 1e3)
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -272,7 +358,7 @@ def main(argv=None):
     fl_attn = attn_flops(sh)
     fl_gate = gate_flops(sh)
     by = stage_bytes(sh)
-    attn_tflops = fl_attn / (mean["attn"] * 1e-6) / 1e12
+    attn_tflops = fl_attn / (attn_avg_us * 1e-6) / 1e12
     traffic = load_traffic()
     roofline = {
         "kernel": "attn_bf16_kernel<128>",
@@ -283,7 +369,8 @@ def main(argv=None):
         "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic,
         "flops_per_launch": fl_attn,
-        "avg_launch_us": round(mean["attn"], 2),
+        "avg_launch_us": round(attn_avg_us, 2),
+        "launches_timed": len(attn_launch_us),
     }
     stages = {}
     for n in ["gate", "select", "gather", "rope_kv", "attn"]:
@@ -323,6 +410,8 @@ def main(argv=None):
         "gate_pct_hbm_peak": round(100 * by["gate"] / (med["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "gather_pct_hbm_peak": round(100 * by["gather"] / (med["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     print(json.dumps(out), flush=True)
     return 0
 
