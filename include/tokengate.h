@@ -133,8 +133,10 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
  *   idx_local   [sum_b min(k, N_b)] int32 output: prompt b's kept positions,
  *               relative to its start, at offset cu_kept[b].
  *   cu_kept     [batch + 1] int32 output: offsets of each prompt's kept tokens.
- * A prompt whose q_len is out of range, or whose length exceeds max_seqlen,
- * gets -1 in every one of its idx_local entries. */
+ * max_seqlen only chooses the kernel's register footprint: a prompt longer
+ * than it is still ranked exactly (its keys are re-read once per radix pass).
+ * A prompt whose q_len is outside [0, min(k, N_b)] gets -1 in every one of
+ * its idx_local entries; the other prompts are unaffected. */
 TG_API tg_status tg_select_topk_varlen(const float* g, const int32_t* cu_seqlens,
                                        const int32_t* q_lens, int32_t batch,
                                        int64_t max_seqlen, int64_t k, int32_t* idx_local,
