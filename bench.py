@@ -275,8 +275,8 @@ def traffic_summary(fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each
     scaled by what the same counter reads for the 1 GiB calibration kernel."""
     true_bytes = COPY_CAL_ELEMS * 4
-    f_attn, nf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "attn_bf16_kernel")
-    w_attn, nw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "attn_bf16_kernel")
+    f_attn, nf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "attn_bf16")
+    w_attn, nw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "attn_bf16")
     f_cal, _ = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "neg")
     w_cal, _ = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "neg")
     f_scale = true_bytes / (f_cal * 1024.0)
@@ -287,7 +287,7 @@ def traffic_summary(fetch_dir, write_dir):
     sh = SHAPES["qwen1p7b_32k"]
     algo = stage_bytes(sh)["attn"]
     rec = {
-        "kernel": "attn_bf16_kernel<128>",
+        "kernel": "attn_bf16_pp_kernel<128>",
         "workload": "qwen1p7b_32k",
         "kernel_source_sha256_16": _file_sha(ATTN_KERNEL_SOURCE),
         "hbm_bytes_per_launch": round(fetch + write),
@@ -361,7 +361,7 @@ def main(argv=None):
     attn_tflops = fl_attn / (attn_avg_us * 1e-6) / 1e12
     traffic = load_traffic()
     roofline = {
-        "kernel": "attn_bf16_kernel<128>",
+        "kernel": "attn_bf16_pp_kernel<128>",
         "bound": "mfma",
         "achieved": round(attn_tflops, 1),
         "peak": PEAK_BF16_TFLOPS,

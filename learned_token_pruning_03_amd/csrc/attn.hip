@@ -10,11 +10,13 @@
 // accumulator, so it enters the logit inside the MFMA and then takes part in
 // the running maximum and the running sum like any other part of the logit.
 //
-// bf16 kernel (one workgroup = 512 threads = 8 waves, two per SIMD):
-//  * a workgroup owns one query head and a pair of 128-query tiles, tile
-//    (T-1-p) then tile p, so that every workgroup has the same causal work;
-//  * the two 4-wave groups split each tile's key range (group 0 takes the
-//    even 64-key tiles, group 1 the odd ones) and merge their partial
+// Two bf16 kernels share the tile shapes and the MFMA data flow below; the
+// launcher picks attn_bf16_pp_kernel when the gate bias of every kept key fits
+// in LDS (8192 keys at head dim 128, 16384 at 64), attn_bf16_kernel beyond.
+//
+// Common to both (one workgroup = 512 threads = 8 waves, two per SIMD):
+//  * the two 4-wave groups split each query tile's key range (group 0 takes
+//    the even 64-key tiles, group 1 the odd ones) and merge their partial
 //    (max, sum, output) through LDS at the end of the tile;
 //  * inside a group each wave owns 32 queries.  S^T = K Q^T runs on
 //    v_mfma_f32_32x32x16_bf16 with Q held in registers as the B operand, so
@@ -22,15 +24,22 @@
 //    per-lane scalars, and P^T leaves the accumulators directly as the B
 //    operand of O^T = V^T P^T (no LDS round trip for P);
 //  * K and V tiles go from global memory straight into LDS (global_load_lds,
-//    XOR-swizzled 256-byte rows, double-buffered per group, the two stages in
-//    separate LDS objects so that reads of one stage never wait for the
-//    loads into the other); the V^T operand is read with ds_read_b64_tr_b16,
-//    the transposing LDS read, so V needs no transposition pass;
-//  * the causal test runs only on tiles reaching past a wave's first query,
-//    comparing original positions; earlier keys are visible because positions
-//    increase with the kept index;
+//    XOR-swizzled 256-byte rows); the V^T operand is read with
+//    ds_read_b64_tr_b16, the transposing LDS read, so V needs no
+//    transposition pass;
+//  * the causal test runs only on tiles reaching past a wave's first query;
+//  * the online softmax keeps a reference maximum per query that only moves
+//    when a logit exceeds it by more than 8 (log2 units), so the O rescale is
+//    skipped on almost every tile;
 //  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
 //    the same XCD, where they share that head's K/V in L2.
+// attn_bf16_kernel (streaming bias): a workgroup owns a pair of query tiles,
+// (T-1-p) then p, so every workgroup has the same causal work; each step
+// copies the next key tile and its bias and positions, computes, then waits.
+// attn_bf16_pp_kernel (ping-pong): one query tile per workgroup, longest
+// first; the two groups alternate MFMA and VALU slots so that the two waves
+// of a SIMD overlap matrix and vector work, with copies issued three slots
+// ahead (see the kernel's own comment).
 #include <cmath>
 
 #include "tg_internal.h"
@@ -268,7 +277,21 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
           mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
         const float m_new = fmaxf(m, mloc * a.scale_log2);
-        const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+        // The reference maximum m is only moved when some lane's logits exceed
+        // it by more than 8 (log2 units): until then p = 2^(t - m) <= 256, which
+        // fp32 accumulators and bf16 weights hold exactly as well as p <= 1,
+        // and numerator and denominator share the same shift.  This skips the
+        // O rescale on most tiles.
+        if (__any(m_new > m + 8.0f)) {
+          const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+          lsum *= alpha;
+#pragma unroll
+          for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+          m = m_new;
+        }
+        const float msub = (m == -INFINITY) ? 0.0f : m;
         float psum = 0.0f;
         bf16x8 pf[4];
 #pragma unroll
@@ -279,16 +302,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
             psum += p;
             pf[kb][e] = (__bf16)p;
           }
-        // Rescale only when some lane's running maximum moved (else the factor is exactly 1).
-        if (__any(m_new > m)) {
-          const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - msub);
-          lsum *= alpha;
-#pragma unroll
-          for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-          m = m_new;
-        }
         lsum += psum;
         // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -354,6 +367,391 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 ping-pong kernel, used when the bias of every kept key fits in LDS.
+//
+// Same workgroup shape and key split as attn_bf16_kernel (8 waves, group g
+// takes the key tiles kt = 2t + g), but the two waves on each SIMD (one per
+// group) never run the same kind of work at the same time.  Work is cut into
+// slots separated by workgroup barriers.  Each group alternates
+//   MFMA slot t:  O^T += V^T P^T for its tile t-1, then S^T = K Q^T for tile t
+//   VALU slot t:  online softmax of tile t (P^T for the next MFMA slot)
+// and group 1 runs one slot behind group 0, so in every slot one wave of each
+// SIMD feeds the matrix core while the other runs the exp/max/sum VALU work.
+// K and V have their own double buffers: K(t+2) and V(t+1) are copied in at
+// the start of VALU slot t, three slots before they are read.  The gate bias
+// of every key is computed once per workgroup into LDS, so the pipelined
+// region holds no register loads from global memory at all.  Keys are
+// visible when their kept index is at most the query's: with strictly
+// increasing positions (the contract of the entry point) that is the same
+// test as comparing positions.
+template <int DH>
+struct PPCfg {
+  static constexpr int MAXK = DH == 128 ? 8192 : 16384;  // keys whose bias fits in LDS
+};
+
+template <int DH>
+__global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
+  using C = AttnCfg<DH>;
+  constexpr int KB = C::K_BYTES;  // one group's K (or V) tile
+  constexpr int MAXK = PPCfg<DH>::MAXK;
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_s0[2 * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_s1[2 * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_s0[2 * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_s1[2 * KB];
+  __shared__ __attribute__((aligned(16))) float bias_all[MAXK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int w4 = wave & 3;
+  const int gtid = tid & 255;
+  const int half = lane >> 5;
+  const int r32 = lane & 31;
+
+  // One 128-query tile per workgroup, tiles in decreasing order of causal
+  // work (all heads of the last tile first).  The first wave of workgroups
+  // fills the chip with the long tiles and each CU that finishes takes the
+  // next shorter one, which pairs long and short tiles per CU without a loop
+  // over two tiles.  rr = blockIdx % hq runs over the KV heads first, so all
+  // query heads of a KV head land on one XCD and share its K/V in L2.
+  const int hq = a.hq, hkv = a.hkv, group = hq / hkv;
+  const int rr = blockIdx.x % hq;
+  const int kvh = rr % hkv;
+  const int head = kvh * group + rr / hkv;
+  int64_t s0 = 0;
+  int L = a.total;
+  if (a.cu) {
+    s0 = a.cu[blockIdx.y];
+    L = a.cu[blockIdx.y + 1] - (int)s0;
+  }
+  const int ntiles = (L + C::BM - 1) / C::BM;
+  const int mt = ntiles - 1 - (int)(blockIdx.x / hq);
+  if (mt < 0) return;
+
+  const uint8_t* kbase = a.k + ((s0 * hkv + kvh) * DH) * 2;
+  const uint8_t* vbase = a.v + ((s0 * hkv + kvh) * DH) * 2;
+  const uint32_t kvs = (uint32_t)((int64_t)hkv * DH * 2);  // bytes between consecutive keys
+  const float c = a.scale_log2;
+
+  const int row0 = mt * C::BM;
+  const int qi = row0 + w4 * 32 + r32;
+  const int qrow = qi < L ? qi : L - 1;
+  const int kend = min(L, row0 + C::BM);
+  const int n_kt = (kend + BN - 1) / BN;
+  const int niter = grp == 0 ? (n_kt + 1) / 2 : n_kt / 2;  // this group's tiles, kt = 2t + grp
+  const int niter0 = (n_kt + 1) / 2;                        // group 0 has at least as many
+
+  // Copy i of this thread fills chunk P = i*256 + gtid of a tile: row
+  // r = P / CPR = i*(256/CPR) + gtid/CPR, stored slot gtid % CPR, holding
+  // logical chunk slot ^ swz(r).  Both swizzles depend only on bits of r that
+  // i does not touch.  The byte offset of copy i from the tile's first key is
+  // fixed per lane; the tile's own offset kt*BN*kvs goes into the scalar base.
+  // K/V bytes of one head span less than 2^31 (checked by the host).
+  const int dma_r0 = gtid / C::CPR;
+  uint32_t off_k[C::DMA], off_v[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const uint32_t rb = (uint32_t)(i * (256 / C::CPR) + dma_r0) * kvs;
+    off_k[i] = rb + (uint32_t)(((gtid % C::CPR) ^ C::swz_k(dma_r0)) * 16);
+    off_v[i] = rb + (uint32_t)(((gtid % C::CPR) ^ C::swz_v(dma_r0)) * 16);
+  }
+  auto lds_addr = [](uint8_t* ptr) __attribute__((always_inline)) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ptr;
+  };
+  const uint32_t k_addr[2] = {lds_addr(k_s0) + grp * KB, lds_addr(k_s1) + grp * KB};
+  const uint32_t v_addr[2] = {lds_addr(v_s0) + grp * KB, lds_addr(v_s1) + grp * KB};
+  auto issue = [&](const uint8_t* base, const uint32_t* off, int kt, uint32_t dst) __attribute__((always_inline)) {
+    const uint8_t* tb = base + (size_t)((uint32_t)(kt * BN) * kvs);
+    if ((kt + 1) * BN <= L) {
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) dma16_sv(tb, off[i], dst + (i * 256 + w4 * 64) * 16);
+    } else {  // last, partial tile: rows past the prompt re-read its last key
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        const int r = kt * BN + i * (256 / C::CPR) + dma_r0;
+        const uint32_t o = off[i] - (uint32_t)(max(r - (L - 1), 0)) * kvs;
+        dma16_sv(tb, o, dst + (i * 256 + w4 * 64) * 16);
+      }
+    }
+  };
+
+  // ---- prologue: Q fragments and gate values (register loads) first, then
+  // the first copies, so the register loads can be waited for while the
+  // copies keep landing.
+  const uint8_t* qp = a.q + (((s0 + qrow) * hq + head) * DH) * 2;
+  bf16x8 qf[DH / 16];
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (ks * 16 + half * 8) * 2);
+  // Bias table, in units of the raw score (log2 g / c), for every key this
+  // query tile can see (rounded up to whole key tiles); keys past the prompt
+  // get -inf.
+  const int nb = n_kt * BN;
+  constexpr int GPT = (MAXK + 511) / 512;
+  float gv[GPT];
+  // Unconditional loads at a clamped index: a predicated load would let the
+  // compiler sink each log2 into its own branch and wait for every load in turn.
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) gv[i] = a.g[s0 + min(tid + 512 * i, L - 1)];
+  // Copies per wave in batch b (K of tile b+2, V of tile b+1); here go batch
+  // -2 (K(0)) and batch -1 (K(1), V(0)).
+  if (0 < niter) issue(kbase, off_k, grp, k_addr[0]);
+  if (1 < niter) issue(kbase, off_k, 2 + grp, k_addr[1]);
+  if (0 < niter) issue(vbase, off_v, grp, v_addr[0]);
+  {
+    const int nc = (0 < niter ? 2 * C::DMA : 0) + (1 < niter ? C::DMA : 0);
+    if (nc == 3 * C::DMA)
+      wait_vm<3 * C::DMA>();  // Q and g have landed; the copies may not have
+    else if (nc == 2 * C::DMA)
+      wait_vm<2 * C::DMA>();
+    else
+      wait_vm<0>();
+  }
+  {
+    const float inv_c = 1.0f / c;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int j = tid + 512 * i;
+      if (j < nb) bias_all[j] = j < L ? log2f(fmaxf(gv[i], kFltMin)) * inv_c : -INFINITY;
+    }
+  }
+  const int G = lane >> 4, ia = (lane >> 2) & 3, ib = lane & 3;
+  // K fragment offset of k-step ks is koff0 ^ (ks << 5) and the V^T offset of
+  // 32-row block md is voff0 ^ (md << 6): the swizzle XOR and the step land
+  // in disjoint bits, for both head sizes.
+  const uint32_t koff0 = r32 * C::ROW + ((half ^ C::swz_k(r32)) * 16);
+  const int vrow = 4 * (G >> 1) + ia;
+  const uint32_t voff0 = vrow * C::ROW + (((2 * (G & 1) + (ib >> 1)) ^ C::swz_v(vrow)) * 16) + (ib & 1) * 8;
+  // Group 1 keeps its O^T blocks in swapped halves: its oacc[md] holds d-block
+  // md ^ MD/2.  Then both groups keep oacc[0, MD/2) and hand over
+  // oacc[MD/2, MD) in the final merge with compile-time indices only (a
+  // runtime index would move the accumulators to scratch memory).
+  const int mdx = grp == 0 ? 0 : C::MD / 2;
+  __syncthreads();  // bias table complete
+
+  {
+    auto batch_count = [&](int b) __attribute__((always_inline)) {
+      return ((b + 2 < niter) ? C::DMA : 0) + ((b + 1 >= 0 && b + 1 < niter) ? C::DMA : 0);
+    };
+
+    float m = -INFINITY;
+    float lsum = 0.0f;
+    f32x16 oacc[C::MD];
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
+    f32x16 sacc[2];
+    bf16x8 pf[4];
+
+    // K(t) and V(t-1) came with batch t-2; batch t-1 may still be landing.
+    auto wait_for_tile = [&](int t) __attribute__((always_inline)) {
+      const int nf = batch_count(t - 1);
+      if (nf == 2 * C::DMA)
+        wait_vm<2 * C::DMA>();
+      else if (nf == C::DMA)
+        wait_vm<C::DMA>();
+      else
+        wait_vm<0>();
+    };
+    // MFMA slot t: O^T += V^T P^T for tile t-1, then S^T = bias + K Q^T for
+    // tile t.  Operand fragments are double-buffered one block ahead: the
+    // LDS reads for block i+1 are issued before the MFMAs of block i, so the
+    // matrix core does not wait out an LDS latency per instruction.
+    // sched_barrier(0) pins that order.
+    auto mfma_slot = [&](int t) __attribute__((always_inline)) {
+      if (t >= 1 && t - 1 < niter) {
+        const uint8_t* vs = ((t - 1) & 1 ? v_s1 : v_s0) + grp * KB;
+        bf16x8 vf[2][C::MD];
+        auto load_v = [&](int kb, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+          for (int md = 0; md < C::MD; ++md) {
+            const uint8_t* vp = vs + (voff0 ^ ((md ^ mdx) << 6)) + (16 * kb) * C::ROW;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * C::ROW));
+            dst[md] = __builtin_bit_cast(
+                bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          }
+        };
+        load_v(0, vf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          if (kb + 1 < 4) load_v(kb + 1, vf[(kb + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int md = 0; md < C::MD; ++md)
+            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb & 1][md], pf[kb], oacc[md], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (t < niter) {
+        const int kt = 2 * t + grp;
+        const uint8_t* ksb = (t & 1 ? k_s1 : k_s0) + grp * KB;
+        const float* bias = bias_all + kt * BN;
+        bf16x8 kf[2][2][2];  // [buffer][k-step within the pair][32-key half]
+        auto load_k = [&](int kp, bf16x8 (*dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              dst[u][mb] = *reinterpret_cast<const bf16x8*>(ksb + mb * 32 * C::ROW + (koff0 ^ ((2 * kp + u) << 5)));
+        };
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const f32x4 bj = *reinterpret_cast<const f32x4*>(bias + mb * 32 + 8 * rq + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[mb][4 * rq + e] = bj[e];
+          }
+        load_k(0, kf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kp = 0; kp < DH / 32; ++kp) {
+          if (kp + 1 < DH / 32) load_k(kp + 1, kf[(kp + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kp & 1][u][mb], qf[2 * kp + u], sacc[mb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    // VALU slot t: copies for later tiles, then the online softmax of tile t.
+    auto valu_slot = [&](int t) __attribute__((always_inline)) {
+      if (t < 0) return;
+      if (t + 2 < niter) issue(kbase, off_k, 2 * (t + 2) + grp, k_addr[t & 1]);
+      if (t + 1 < niter) issue(vbase, off_v, 2 * (t + 1) + grp, v_addr[(t + 1) & 1]);
+      if (t >= niter) return;
+      const int kt = 2 * t + grp;
+      if (kt * BN + BN - 1 > row0 + w4 * 32) {  // tile reaches past this wave's first query
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = kt * BN + mb * 32 + 8 * rq + 4 * half + e;
+              sacc[mb][4 * rq + e] = j > qi ? -INFINITY : sacc[mb][4 * rq + e];
+            }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mb][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_new = fmaxf(m, mloc * c);
+      // The reference maximum only moves when some lane's logits exceed it by
+      // more than 8 (log2 units); until then p <= 256, which the fp32
+      // accumulators and bf16 weights hold as well as p <= 1, and numerator
+      // and denominator share the shift.
+      if (__any(m_new > m + 8.0f)) {
+        const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+        m = m_new;
+      }
+      const float msub = (m == -INFINITY) ? 0.0f : m;
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + e], c, -msub));
+          psum += p;
+          pf[kb][e] = (__bf16)p;
+        }
+      lsum += psum;
+    };
+
+    // Slot pairs u = 0..niter0.  Group 0: MFMA slot u, then VALU slot u.
+    // Group 1, one slot behind: VALU slot u-1, then MFMA slot u.  Both groups
+    // meet the same two barriers per pair.
+    if (grp == 0) {
+      for (int u = 0; u <= niter0; ++u) {
+        wait_for_tile(u);
+        plain_barrier();
+        mfma_slot(u);
+        plain_barrier();
+        valu_slot(u);
+      }
+    } else {
+      for (int u = 0; u <= niter0; ++u) {
+        plain_barrier();
+        valu_slot(u - 1);
+        wait_for_tile(u);
+        plain_barrier();
+        mfma_slot(u);
+      }
+    }
+
+    // ---- merge the two groups' partial results, normalise, store ----
+    // Group 0 finishes d-blocks md < MD/2, group 1 blocks md >= MD/2: each
+    // hands the other half of its partial O^T (and its m, l) across LDS.
+    __syncthreads();
+    constexpr int HM = C::MD / 2;
+    float* to_g0 = reinterpret_cast<float*>(k_s0);  // group 1's rows md < HM
+    float* to_g1 = reinterpret_cast<float*>(k_s1);  // group 0's rows md >= HM
+    float* scr_m = reinterpret_cast<float*>(v_s0);
+    float* scr_l = scr_m + 8 * 64;
+    {
+      float* out = grp == 0 ? to_g1 : to_g0;
+#pragma unroll
+      for (int h = 0; h < HM; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out[(w4 * (HM * 16) + h * 16 + r) * 64 + lane] = oacc[HM + h][r];
+      scr_m[wave * 64 + lane] = m;
+      scr_l[wave * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    {
+      const float m1 = scr_m[(wave ^ 4) * 64 + lane];
+      const float l1 = scr_l[(wave ^ 4) * 64 + lane];
+      const float mt_ = fmaxf(m, m1);
+      const float a0 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mt_);
+      const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - mt_);
+      float l = lsum * a0 + l1 * a1;
+      l += __shfl_xor(l, 32, kWave);
+      const float inv = 1.0f / l;
+      const float* in = grp == 0 ? to_g0 : to_g1;
+      const int md0 = grp == 0 ? 0 : HM;
+      if (qi < L) {
+        uint8_t* op = a.o + (((s0 + qi) * hq + head) * DH) * 2;
+#pragma unroll
+        for (int h = 0; h < HM; ++h) {
+          const f32x16& keep = oacc[h];
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            float ov[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rq + e;
+              ov[e] = (keep[r] * a0 + in[(w4 * (HM * 16) + h * 16 + r) * 64 + lane] * a1) * inv;
+            }
+            const u32x2 packed = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+            *reinterpret_cast<u32x2*>(op + ((md0 + h) * 32 + 8 * rq + 4 * half) * 2) = packed;
+          }
+        }
+        if (a.lse && grp == 0 && half == 0) a.lse[(int64_t)head * a.total + s0 + qi] = (mt_ + log2f(l)) * kLn2;
+      }
+    }
   }
 }
 
@@ -458,10 +856,22 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   const int64_t ntiles = (max_seqlen + 127) / 128;
   const int64_t npairs = (ntiles + 1) / 2;
   const dim3 grid((unsigned)(npairs * hq), cu_seqlens ? (unsigned)batch : 1u);
-  if (dh == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
+  // The ping-pong kernel keeps a bias entry per key (rounded up to a 64-key
+  // tile) in LDS and takes one query tile per workgroup; longer prompts take
+  // the streaming-bias kernel, two tiles per workgroup.
+  const int64_t keys = (max_seqlen + 63) / 64 * 64;
+  const dim3 grid_pp((unsigned)(ntiles * hq), cu_seqlens ? (unsigned)batch : 1u);
+  if (dh == 128) {
+    if (keys <= PPCfg<128>::MAXK)
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, grid_pp, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
+  } else {
+    if (keys <= PPCfg<64>::MAXK)
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, grid_pp, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -33,22 +33,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's bytes land at
-// LDS address m0 + 16 l.  Written as asm so that the compiler's wait-count
-// pass does not track it: it would otherwise drain all outstanding copies
-// before reading any stage of the ring.  The instruction has no register
-// results; completion is ordered by the explicit vmcnt waits below.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
-}
-
-// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= v, nothing else.
-template <int V>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(V >= 0 && V < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (V & 15) | ((V >> 4) << 14));
-}
-
 template <int H>
 __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int n, int d, const uint16_t* __restrict__ w1,
@@ -151,10 +135,9 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
       wait_vm<PER_CHUNK>();  // chunk kt+1 may still be landing
     else
       wait_vm<0>();
-    // Every wave has waited for its own share of chunk kt.  A plain barrier
-    // (no release fence) keeps chunks kt+1 and kt+2 in flight across it; the
-    // memory clobber stops the compiler moving LDS accesses over it.
-    asm volatile("s_barrier" ::: "memory");
+    // Every wave has waited for its own share of chunk kt; chunks kt+1 and
+    // kt+2 stay in flight across the barrier.
+    plain_barrier();
     if (kt + 2 < nk) issue(kt + 2, nxt2);
     compute(cur);
   };

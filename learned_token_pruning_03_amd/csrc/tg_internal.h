@@ -33,6 +33,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's bytes land at
+// LDS address m0 + 16 l.  Written as asm so that the compiler's wait-count
+// pass does not track it: once copies stay in flight across a loop back-edge
+// that pass loses track of which LDS buffer they target and drains all of
+// them before any LDS read.  The instruction has no register results; the
+// caller orders completion with explicit vmcnt waits (wait_vm).  A
+// compiler-visible global load issued while such copies are in flight gets a
+// wait that also drains them, so loops built on dma16 keep all other global
+// loads outside the pipelined region.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// Same copy from a wave-uniform 64-bit base (scalar registers) plus a 32-bit
+// per-lane byte offset: one vector register per copy instead of two.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 layout) that waits for vmcnt <= v, nothing else.
+template <int V>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (V & 15) | ((V >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads: the
+// fence would wait for every outstanding global->LDS copy.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -315,6 +315,21 @@ def test_attn_bf16_full_size_sampled_rows(gpu_lib, name, gkind):
     assert np.all(np.isfinite(o))
 
 
+@pytest.mark.parametrize("n,dh", [(8300, 128), (16500, 64)])
+def test_attn_bf16_past_the_lds_bias_table(gpu_lib, n, dh):
+    """Kept counts above the ping-pong kernel's LDS bias table (8192 keys at
+    head dim 128, 16384 at 64) take the streaming-bias kernel."""
+    _say("attn long prompt", n, dh)
+    q, k, v, g, pos = _attn_inputs(n, 2, 1, dh, torch.bfloat16, 31, "wide")
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    rows = _sample_rows(n, 6, count=48)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy(), rows=rows)
+    err = float(np.max(np.abs(o[rows] - wo)))
+    _say("  max abs err o", err)
+    assert err <= 2e-2
+    assert np.max(np.abs(lse[:, rows] - wl)) <= 1e-3
+
+
 def test_attn_varlen_ragged(gpu_lib):
     lens = [256, 1, 100, 256, 129, 0, 256]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
