@@ -84,15 +84,19 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
             (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
 
-  auto issue = [&](int kt, uint8_t* sb) __attribute__((always_inline)) {
+  // Copy q of this wave for chunk kt into stage sb: h blocks first, then W1.
+  auto issue_one = [&](int q, int kt, uint8_t* sb) __attribute__((always_inline)) {
     const int koff = kt * (kGateBK * 2);
     const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)sb;
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) dma16(pa[i] + koff, base + (NW * i + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) dma16(pb[i] + koff, base + H_BYTES + (NW * i + wave) * 1024);
+    if (q < A_DMA)
+      dma16(pa[q] + koff, base + (NW * q + wave) * 1024);
+    else
+      dma16(pb[q - A_DMA] + koff, base + H_BYTES + (NW * (q - A_DMA) + wave) * 1024);
   };
-
+  auto issue = [&](int kt, uint8_t* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < PER_CHUNK; ++q) issue_one(q, kt, sb);
+  };
   f32x16 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -107,7 +111,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
   // This wave takes sub-steps 2 kh and 2 kh + 1 of every 64-wide chunk; its
   // partner (same tile, other kh) takes the other two.  Both fragment sets are
   // read before the first MFMA; the second wave on the SIMD covers the wait.
-  auto compute = [&](const uint8_t* base) __attribute__((always_inline)) {
+  // The copies of chunk kt_next (if any) are spread between the MFMAs, one
+  // after every second MFMA: issued all at once, the eight waves' copies queue
+  // up in the address unit and hold back the MFMAs of the later waves.
+  auto compute = [&](const uint8_t* base, int kt_next, uint8_t* sb_next) __attribute__((always_inline)) {
     bf16x8 af[2][MT], bfr[2][NT];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -119,13 +126,24 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
       for (int j = 0; j < NT; ++j)
         bfr[u][j] = *reinterpret_cast<const bf16x8*>(base + H_BYTES + swz(wn * (H / 2) + j * 32 + r32, chunk));
     }
+    const bool copy = kt_next >= 0;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < NT; ++j) {
+          const int mi = (u * MT + i) * NT + j;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u][i], bfr[u][j], acc[i][j], 0, 0, 0);
+          if ((mi & 1) && (mi >> 1) < PER_CHUNK) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (copy) issue_one(mi >> 1, kt_next, sb_next);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+    for (int q = MT * NT; q < PER_CHUNK; ++q)  // copies left over when there are few MFMAs
+      if (copy) issue_one(q, kt_next, sb_next);
   };
 
   // One ring step: chunk kt sits in stage `cur`; chunk kt+2 goes to `nxt2`,
@@ -138,8 +156,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     // Every wave has waited for its own share of chunk kt; chunks kt+1 and
     // kt+2 stay in flight across the barrier.
     plain_barrier();
-    if (kt + 2 < nk) issue(kt + 2, nxt2);
-    compute(cur);
+    compute(cur, kt + 2 < nk ? kt + 2 : -1, nxt2);
   };
 
   const int nk = d / kGateBK;
