@@ -40,6 +40,8 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="qwen1p7b_32k", choices=["qwen1p7b_32k", "qwen1p7b_128k", "stack19"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-full-context", action="store_true",
+                   help="skip the comparison with one ungated layer over all N tokens")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the run, launch a plain 1 GiB -> 1 GiB streaming kernel (torch.neg on fp32) "
@@ -174,6 +176,34 @@ def time_stages(path, reps):
             samples[n].append(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3)  # us
         path.step_no += 1
     return {n: statistics.median(v) for n, v in samples.items()}, {n: sum(v) / len(v) for n, v in samples.items()}
+
+
+def full_context(tg, W, sh, dev, reps=8):
+    """One upper layer without pruning: RoPE + KV cache and ungated causal GQA
+    attention over all N prompt tokens (the same layer shape), medians of
+    event-timed repetitions.  The pruned path runs the same two stages on K."""
+    import torch
+    q, k, v = W.qkv(sh.n, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 7)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    kc, vc, o = torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
+    pos = torch.arange(sh.n, dtype=torch.int32, device=dev)
+    table = tg.tg_rope_table(sh.n, sh.dh, sh.rope_base, dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    rope_t, attn_t = [], []
+    for r in range(reps + 1):
+        ev[0].record()
+        tg.tg_rope_kv(q, k, v, pos, table, k_cache=kc, v_cache=vc)
+        ev[1].record()
+        tg.tg_gated_attn(q, kc, vc, None, pos, o=o)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if r:
+            rope_t.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            attn_t.append(ev[1].elapsed_time(ev[2]) * 1e3)
+    flops = 4.0 * sh.dh * sh.hq * sh.n * (sh.n + 1) / 2.0
+    a = statistics.median(attn_t)
+    return {"n": sh.n, "rope_kv_us": round(statistics.median(rope_t), 2), "attn_us": round(a, 2),
+            "attn_TFLOP/s": round(flops / (a * 1e-6) / 1e12, 1)}
 
 
 def cpu_baseline(W, name):
@@ -382,6 +412,17 @@ def main(argv=None):
             e["TFLOP/s"] = round(fl_attn / (med[n] * 1e-6) / 1e12, 1)
         stages[n] = e
 
+    full = None
+    if not args.no_full_context:
+        print("[bench] timing one ungated layer over all N tokens ...", file=sys.stderr, flush=True)
+        full = full_context(tg, W, sh, dev)
+        layer_gated = med["rope_kv"] + med["attn"]
+        full["layer_us"] = round(full["rope_kv_us"] + full["attn_us"], 2)
+        full["layer_speedup_vs_pruned"] = round(full["layer_us"] / layer_gated, 2)
+        # One selection layer's overhead (gate, select, gather) is paid once per
+        # prompt; every upper layer then runs on K tokens instead of N.
+        full["pruning_overhead_us"] = round(med["gate"] + med["select"] + med["gather"], 2)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
@@ -406,6 +447,7 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "full_context": full,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "gate_pct_hbm_peak": round(100 * by["gate"] / (med["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "gather_pct_hbm_peak": round(100 * by["gather"] / (med["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),

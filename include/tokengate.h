@@ -212,7 +212,9 @@ TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t 
  *   hq,hkv  heads; hq % hkv == 0.     dh: 64 or 128.
  *   scale   logit scale (1/sqrt(dh) for the standard form); must be > 0.
  *   q       [n_kept, hq, dh] (rotated); k, v [n_kept, hkv, dh] (the cache).
- *   g       [n_kept] fp32 gate values of the kept tokens.
+ *   g       [n_kept] fp32 gate values of the kept tokens, or NULL for no gate
+ *           (every key weighs 1: plain causal GQA attention, the form of the
+ *           full-context layers at or below the selection layer).
  *   pos     [n_kept] int32 original positions, strictly increasing (the
  *           order select + gather produce).  Precondition, not checked.
  *   o       [n_kept, hq, dh] output, dtype.
@@ -233,6 +235,28 @@ TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
                                       const void* q, const void* k, const void* v,
                                       const float* g, const int32_t* pos, void* o,
                                       float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Gated attention with a per-head gain on the gate bias.  [paper] Abstract
+ * and the page's discussion of the bias: each head scales the importance
+ * bias with its own gain and a temperature, whose exact forms the pages do not
+ * print.  This library's reading: head h uses the bias
+ *     gamma_h * ln max(g_j, FLT_MIN),     gamma_h = head_gain[h]
+ * (gain over temperature, any finite value; gamma_h = 0 switches the gate off
+ * for that head, gamma_h = 1 is tg_gated_attn).
+ *
+ *   cu_seqlens  [batch + 1] int32 (device) for a packed ragged batch, as in
+ *               tg_gated_attn_varlen; or NULL for one prompt of `total` rows
+ *               (batch and max_seqlen are then ignored).
+ *   g           [total] fp32, or NULL for no gate.
+ *   head_gain   [hq] fp32 (device), or NULL for gamma_h = 1.
+ *   Other arguments and errors as tg_gated_attn_varlen.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                  int64_t max_seqlen, int64_t total, int32_t hq, int32_t hkv,
+                                  int32_t dh, float scale, const void* q, const void* k,
+                                  const void* v, const float* g, const float* head_gain,
+                                  const int32_t* pos, void* o, float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

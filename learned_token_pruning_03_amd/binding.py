@@ -48,6 +48,8 @@ SIGNATURES = {
                        _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_gated_attn_varlen": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32,
                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_gated_attn_ex": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp,
+                          _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -223,42 +225,62 @@ def tg_rope_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Ten
     return q, k_cache, v_cache
 
 
-def tg_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, pos: torch.Tensor,
+def tg_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor], pos: torch.Tensor,
                   scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None, want_lse: bool = False):
-    """Token-gated causal GQA attention; returns o (and lse [hq, n] if requested)."""
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                  head_gain: Optional[torch.Tensor] = None):
+    """Token-gated causal GQA attention; returns o (and lse [hq, n] if requested).
+
+    g=None: no gate (plain causal attention).  head_gain: [hq] fp32 multiplier
+    of the gate bias per query head (tg_gated_attn_ex)."""
     lib = load_library()
     n, hq, dh = q.shape
     hkv = k.shape[1]
     _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
-    _need(g.dtype == torch.float32 and pos.dtype == torch.int32, "g is fp32 and pos int32")
+    _need((g is None or g.dtype == torch.float32) and pos.dtype == torch.int32, "g is fp32 and pos int32")
+    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
+          "head_gain is fp32 [hq]")
     if scale is None:
         scale = dh ** -0.5
     if o is None:
         o = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty(hq, n, dtype=torch.float32, device=q.device)
-    _check("tg_gated_attn", lib.tg_gated_attn(_dtype_code(q), n, hq, hkv, dh, float(scale), _ptr(q), _ptr(k),
-                                              _ptr(v), _ptr(g), _ptr(pos), _ptr(o), _ptr(lse), _stream(q)))
+    if g is None or head_gain is not None:
+        _check("tg_gated_attn_ex",
+               lib.tg_gated_attn_ex(_dtype_code(q), None, 1, n, n, hq, hkv, dh, float(scale), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(g), _ptr(head_gain), _ptr(pos), _ptr(o), _ptr(lse), _stream(q)))
+    else:
+        _check("tg_gated_attn", lib.tg_gated_attn(_dtype_code(q), n, hq, hkv, dh, float(scale), _ptr(q), _ptr(k),
+                                                  _ptr(v), _ptr(g), _ptr(pos), _ptr(o), _ptr(lse), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o
 
 
-def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, pos: torch.Tensor,
-                         cu_seqlens: torch.Tensor, max_seqlen: int, scale: Optional[float] = None,
-                         o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                         want_lse: bool = False):
+def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                         pos: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                         scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                         head_gain: Optional[torch.Tensor] = None):
     lib = load_library()
     total, hq, dh = q.shape
     hkv = k.shape[1]
     batch = cu_seqlens.numel() - 1
+    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
+          "head_gain is fp32 [hq]")
     if scale is None:
         scale = dh ** -0.5
     if o is None:
         o = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty(hq, total, dtype=torch.float32, device=q.device)
-    _check("tg_gated_attn_varlen",
-           lib.tg_gated_attn_varlen(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv, dh,
-                                    float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(pos), _ptr(o), _ptr(lse),
-                                    _stream(q)))
+    if g is None or head_gain is not None:
+        _check("tg_gated_attn_ex",
+               lib.tg_gated_attn_ex(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv, dh,
+                                    float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(head_gain), _ptr(pos),
+                                    _ptr(o), _ptr(lse), _stream(q)))
+    else:
+        _check("tg_gated_attn_varlen",
+               lib.tg_gated_attn_varlen(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv,
+                                        dh, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(pos), _ptr(o),
+                                        _ptr(lse), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o

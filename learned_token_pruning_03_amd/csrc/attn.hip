@@ -51,7 +51,8 @@ struct AttnArgs {
   const uint8_t* q;
   const uint8_t* k;
   const uint8_t* v;
-  const float* g;
+  const float* g;          // gate values, or NULL: no gate (every key weighs 1)
+  const float* head_gain;  // [hq] multiplier of the gate bias, or NULL: 1
   const int32_t* pos;
   uint8_t* o;
   float* lse;
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   // staged in registers; K and V go straight from global memory to LDS.
   float breg = 0.0f;
   int preg = 0;
-  const float inv_c = 1.0f / a.scale_log2;
+  // Gate bias in units of the raw score, times the head's gain.
+  const float inv_c = (a.head_gain ? a.head_gain[head] : 1.0f) / a.scale_log2;
   // Direct load i of this thread fills LDS chunk P = i*256 + gtid of the tile:
   // row P / CPR, stored position P % CPR, holding logical chunk pos ^ swz(row).
   uint32_t dma_k[C::DMA], dma_v[C::DMA];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     if (gtid < C::BN) {
       const int j = kt * C::BN + gtid;
       if (j < L) {
-        breg = a.g[s0 + j];
+        breg = a.g ? a.g[s0 + j] : 1.0f;
         preg = a.pos[s0 + j];
       } else {
         breg = -INFINITY;
@@ -438,6 +440,10 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   const uint8_t* vbase = a.v + ((s0 * hkv + kvh) * DH) * 2;
   const uint32_t kvs = (uint32_t)((int64_t)hkv * DH * 2);  // bytes between consecutive keys
   const float c = a.scale_log2;
+  const bool has_gate = a.g != nullptr;
+  // Read before any copy is in flight: a register load waited for later would
+  // also wait for the copies.
+  const float gain = a.head_gain ? a.head_gain[head] : 1.0f;
 
   const int row0 = mt * C::BM;
   const int qi = row0 + w4 * 32 + r32;
@@ -497,8 +503,12 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   float gv[GPT];
   // Unconditional loads at a clamped index: a predicated load would let the
   // compiler sink each log2 into its own branch and wait for every load in turn.
+  // Without a gate these loads read the position array instead (same length,
+  // values unused): a NULL test inside the loop would split the loads into
+  // branches that each wait for their own load.
+  const float* gsrc = has_gate ? a.g + s0 : reinterpret_cast<const float*>(a.pos + s0);
 #pragma unroll
-  for (int i = 0; i < GPT; ++i) gv[i] = a.g[s0 + min(tid + 512 * i, L - 1)];
+  for (int i = 0; i < GPT; ++i) gv[i] = gsrc[min(tid + 512 * i, L - 1)];
   // Copies per wave in batch b (K of tile b+2, V of tile b+1); here go batch
   // -2 (K(0)) and batch -1 (K(1), V(0)).
   if (0 < niter) issue(kbase, off_k, grp, k_addr[0]);
@@ -513,8 +523,9 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     else
       wait_vm<0>();
   }
-  {
-    const float inv_c = 1.0f / c;
+  if (!has_gate && tid < BN) bias_all[tid] = 0.0f;
+  if (a.g) {
+    const float inv_c = gain / c;  // gate bias times the head's gain
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
       const int j = tid + 512 * i;
@@ -566,6 +577,9 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     // matrix core does not wait out an LDS latency per instruction.
     // sched_barrier(0) pins that order.
     auto mfma_slot = [&](int t) __attribute__((always_inline)) {
+      // Higher issue priority while this wave feeds the matrix core; the
+      // other wave on the SIMD (in its VALU slot) fills the gaps.
+      __builtin_amdgcn_s_setprio(2);
       if (t >= 1 && t - 1 < niter) {
         const uint8_t* vs = ((t - 1) & 1 ? v_s1 : v_s0) + grp * KB;
         bf16x8 vf[2][C::MD];
@@ -595,7 +609,9 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       if (t < niter) {
         const int kt = 2 * t + grp;
         const uint8_t* ksb = (t & 1 ? k_s1 : k_s0) + grp * KB;
-        const float* bias = bias_all + kt * BN;
+        // Without a gate every tile reads the 64 zeros at the start of the table
+        // (keys past the prompt are then removed by the causal test).
+        const float* bias = bias_all + (has_gate ? kt * BN : 0);
         bf16x8 kf[2][2][2];  // [buffer][k-step within the pair][32-key half]
         auto load_k = [&](int kp, bf16x8 (*dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -626,6 +642,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // VALU slot t: copies for later tiles, then the online softmax of tile t.
     auto valu_slot = [&](int t) __attribute__((always_inline)) {
@@ -763,6 +780,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ k,
                                                       const float* __restrict__ v,
                                                       const float* __restrict__ g,
+                                                      const float* __restrict__ head_gain,
                                                       const int32_t* __restrict__ pos,
                                                       float* __restrict__ o, float* __restrict__ lse,
                                                       const int32_t* __restrict__ cu, int total, int hq,
@@ -782,6 +800,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   }
   const int q0 = blockIdx.x * 64;
   if (q0 >= L) return;
+  const float gain = head_gain ? head_gain[head] : 1.0f;
   const int qi = q0 + lane;
   const int qrow = qi < L ? qi : L - 1;
   float qv[DH];
@@ -804,7 +823,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     }
     {
       const int j = k0 + lane;
-      bs[lane] = j < L ? logf(fmaxf(g[s0 + j], kFltMin)) : -INFINITY;
+      bs[lane] = j < L ? (g ? logf(fmaxf(g[s0 + j], kFltMin)) * gain : 0.0f) : -INFINITY;
       ps[lane] = j < L ? pos[s0 + j] : 0x7fffffff;
     }
     __syncthreads();
@@ -838,13 +857,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch, int64_t max_seqlen,
                             int hq, int hkv, int dh, float scale, const void* q, const void* k,
-                            const void* v, const float* g, const int32_t* pos, void* o, float* lse,
-                            hipStream_t stream) {
+                            const void* v, const float* g, const float* head_gain, const int32_t* pos,
+                            void* o, float* lse, hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint8_t*>(q);
   a.k = static_cast<const uint8_t*>(k);
   a.v = static_cast<const uint8_t*>(v);
   a.g = g;
+  a.head_gain = head_gain;
   a.pos = pos;
   a.o = static_cast<uint8_t*>(o);
   a.lse = lse;
@@ -857,17 +877,18 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   const int64_t npairs = (ntiles + 1) / 2;
   const dim3 grid((unsigned)(npairs * hq), cu_seqlens ? (unsigned)batch : 1u);
   // The ping-pong kernel keeps a bias entry per key (rounded up to a 64-key
-  // tile) in LDS and takes one query tile per workgroup; longer prompts take
-  // the streaming-bias kernel, two tiles per workgroup.
+  // tile) in LDS and takes one query tile per workgroup; without a gate it
+  // needs no table and takes any length.  Longer gated prompts take the
+  // streaming-bias kernel, two tiles per workgroup.
   const int64_t keys = (max_seqlen + 63) / 64 * 64;
   const dim3 grid_pp((unsigned)(ntiles * hq), cu_seqlens ? (unsigned)batch : 1u);
   if (dh == 128) {
-    if (keys <= PPCfg<128>::MAXK)
+    if (!g || keys <= PPCfg<128>::MAXK)
       hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, grid_pp, dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
   } else {
-    if (keys <= PPCfg<64>::MAXK)
+    if (!g || keys <= PPCfg<64>::MAXK)
       hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, grid_pp, dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
@@ -877,15 +898,15 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
 
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch, int64_t max_seqlen,
                            int hq, int hkv, int dh, float scale, const float* q, const float* k,
-                           const float* v, const float* g, const int32_t* pos, float* o, float* lse,
-                           hipStream_t stream) {
+                           const float* v, const float* g, const float* head_gain, const int32_t* pos,
+                           float* o, float* lse, hipStream_t stream) {
   const dim3 grid((unsigned)((max_seqlen + 63) / 64), (unsigned)hq, cu_seqlens ? (unsigned)batch : 1u);
   if (dh == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, pos, o, lse,
-                       cu_seqlens, (int)total, hq, hkv, scale);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos, o,
+                       lse, cu_seqlens, (int)total, hq, hkv, scale);
   else
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, g, pos, o, lse,
-                       cu_seqlens, (int)total, hq, hkv, scale);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos, o,
+                       lse, cu_seqlens, (int)total, hq, hkv, scale);
   return hipGetLastError();
 }
 

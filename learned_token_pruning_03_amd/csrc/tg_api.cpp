@@ -206,7 +206,8 @@ static tg_status check_attn(tg_dtype dtype, int64_t max_rows, int32_t hq, int32_
   if (max_rows * hkv * dh * elem_size(dtype) >= (int64_t(1) << 31))
     return fail(TG_ERR_UNSUPPORTED, "attn: one prompt's K (or V) must be below 2 GiB");
   if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "attn: scale must be > 0");
-  if (!q || !k || !v || !g || !pos || !o) return fail(TG_ERR_INVALID_ARG, "attn: NULL pointer argument");
+  (void)g;  // NULL: no gate
+  if (!q || !k || !v || !pos || !o) return fail(TG_ERR_INVALID_ARG, "attn: NULL pointer argument");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(TG_ERR_INVALID_ARG, "attn: q, k, v and o must be 16-byte aligned");
   return TG_OK;
@@ -215,14 +216,15 @@ static tg_status check_attn(tg_dtype dtype, int64_t max_rows, int32_t hq, int32_
 static hipError_t dispatch_attn(tg_dtype dtype, int64_t total, const int32_t* cu, int batch,
                                 int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
                                 const void* q, const void* k, const void* v, const float* g,
-                                const int32_t* pos, void* o, float* lse, hipStream_t stream) {
+                                const float* head_gain, const int32_t* pos, void* o, float* lse,
+                                hipStream_t stream) {
   if (dtype == TG_BF16)
-    return tg::launch_attn_bf16(total, cu, batch, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o,
-                                lse, stream);
+    return tg::launch_attn_bf16(total, cu, batch, max_seqlen, hq, hkv, dh, scale, q, k, v, g, head_gain,
+                                pos, o, lse, stream);
   return tg::launch_attn_f32(total, cu, batch, max_seqlen, hq, hkv, dh, scale,
                              static_cast<const float*>(q), static_cast<const float*>(k),
-                             static_cast<const float*>(v), g, pos, static_cast<float*>(o), lse,
-                             stream);
+                             static_cast<const float*>(v), g, head_gain, pos, static_cast<float*>(o),
+                             lse, stream);
 }
 
 TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv, int32_t dh,
@@ -233,8 +235,8 @@ TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32
   if (n_kept == 0) return ok();
   tg_status st = check_attn(dtype, n_kept, hq, hkv, dh, scale, q, k, v, g, pos, o);
   if (st != TG_OK) return st;
-  return from_hip(dispatch_attn(dtype, n_kept, nullptr, 1, n_kept, hq, hkv, dh, scale, q, k, v, g, pos,
-                                o, lse, stream),
+  return from_hip(dispatch_attn(dtype, n_kept, nullptr, 1, n_kept, hq, hkv, dh, scale, q, k, v, g, nullptr,
+                                pos, o, lse, stream),
                   "attn");
 }
 
@@ -250,8 +252,30 @@ TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
   if (st != TG_OK) return st;
   if (!cu_seqlens) return fail(TG_ERR_INVALID_ARG, "attn_varlen: NULL cu_seqlens");
   return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
-                                g, pos, o, lse, stream),
+                                g, nullptr, pos, o, lse, stream),
                   "attn_varlen");
+}
+
+TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                  int64_t max_seqlen, int64_t total, int32_t hq, int32_t hkv,
+                                  int32_t dh, float scale, const void* q, const void* k,
+                                  const void* v, const float* g, const float* head_gain,
+                                  const int32_t* pos, void* o, float* lse, hipStream_t stream) {
+  if (total < 0 || total > kMaxI32) return fail(TG_ERR_INVALID_ARG, "attn_ex: total out of range");
+  if (cu_seqlens) {
+    if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32)
+      return fail(TG_ERR_INVALID_ARG, "attn_ex: batch or max_seqlen out of range");
+    if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
+  } else {
+    batch = 1;
+    max_seqlen = total;
+    if (total == 0) return ok();
+  }
+  tg_status st = check_attn(dtype, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o);
+  if (st != TG_OK) return st;
+  return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
+                                g, head_gain, pos, o, lse, stream),
+                  "attn_ex");
 }
 
 }  // extern "C"

@@ -99,10 +99,12 @@ hipError_t launch_rope_kv(int elem_bytes, int64_t n_kept, int hq, int hkv, int d
 hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
                             int64_t max_seqlen, int hq, int hkv, int dh, float scale,
                             const void* q, const void* k, const void* v, const float* g,
-                            const int32_t* pos, void* o, float* lse, hipStream_t stream);
+                            const float* head_gain, const int32_t* pos, void* o, float* lse,
+                            hipStream_t stream);
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
                            int64_t max_seqlen, int hq, int hkv, int dh, float scale,
                            const float* q, const float* k, const float* v, const float* g,
-                           const int32_t* pos, float* o, float* lse, hipStream_t stream);
+                           const float* head_gain, const int32_t* pos, float* o, float* lse,
+                           hipStream_t stream);
 
 }  // namespace tg

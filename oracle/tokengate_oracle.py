@@ -207,18 +207,22 @@ def ref_rope_kv(q, k, v, pos, base: float):
 # the bias stays finite; key j is visible to query i iff pos_j <= pos_i; query
 # head h uses KV head h // (Hq / Hkv).
 # --------------------------------------------------------------------------
-def ref_attn(q, k, v, g, pos, scale: float | None = None, rows=None):
-    """q [n, hq, dh], k/v [n, hkv, dh], g [n], pos [n].
+def ref_attn(q, k, v, g, pos, scale: float | None = None, rows=None, head_gain=None):
+    """q [n, hq, dh], k/v [n, hkv, dh], g [n] or None, pos [n].
 
     Returns (o [n, hq, dh], lse [hq, n]) in float64; lse is the natural-log
     normaliser of the biased logits.  With ``rows`` (query indices) only those
     queries are computed, against all n keys: o [len(rows), hq, dh] and
     lse [hq, len(rows)].
+
+    ``g=None`` is the ungated attention of the full-context layers (bias 0).
+    READING (per-head gain and temperature on the bias, named by the TokenGate
+    paper page without their forms): head h adds ``head_gain[h] * ln max(g_j,
+    FLT_MIN)``; ``head_gain=None`` means 1 for every head.
     """
     q = _f64(q)
     k = _f64(k)
     v = _f64(v)
-    g = _f64(g)
     pos = _i64(pos)
     n, hq, dh = q.shape
     hkv = k.shape[1]
@@ -226,13 +230,14 @@ def ref_attn(q, k, v, g, pos, scale: float | None = None, rows=None):
     if scale is None:
         scale = 1.0 / np.sqrt(dh)
     group = hq // hkv
-    bias = np.log(np.maximum(g, FLT_MIN))                     # [n]
+    bias = np.zeros(n) if g is None else np.log(np.maximum(_f64(g), FLT_MIN))   # [n]
+    gain = np.ones(hq) if head_gain is None else _f64(head_gain)
     visible = pos[None, :] <= pos[rows][:, None]              # [query i, key j]
     o = np.empty((len(rows), hq, dh))
     lse = np.empty((hq, len(rows)))
     for h in range(hq):
         kvh = h // group
-        s = scale * (q[rows, h, :] @ k[:, kvh, :].T) + bias[None, :]
+        s = scale * (q[rows, h, :] @ k[:, kvh, :].T) + gain[h] * bias[None, :]
         s = np.where(visible, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
@@ -242,7 +247,7 @@ def ref_attn(q, k, v, g, pos, scale: float | None = None, rows=None):
     return o, lse
 
 
-def ref_attn_varlen(q, k, v, g, pos, cu_seqlens, scale: float | None = None):
+def ref_attn_varlen(q, k, v, g, pos, cu_seqlens, scale: float | None = None, head_gain=None):
     """Packed variant: each prompt b attends only within its own rows."""
     cu = _i64(cu_seqlens)
     q = _f64(q)
@@ -251,13 +256,14 @@ def ref_attn_varlen(q, k, v, g, pos, cu_seqlens, scale: float | None = None):
     lse = np.empty((hq, n))
     k = _f64(k)
     v = _f64(v)
-    g = _f64(g)
+    g = None if g is None else _f64(g)
     pos = _i64(pos)
     for b in range(len(cu) - 1):
         a, e = cu[b], cu[b + 1]
         if e == a:
             continue
-        ob, lb = ref_attn(q[a:e], k[a:e], v[a:e], g[a:e], pos[a:e], scale)
+        ob, lb = ref_attn(q[a:e], k[a:e], v[a:e], None if g is None else g[a:e], pos[a:e], scale,
+                          head_gain=head_gain)
         o[a:e] = ob
         lse[:, a:e] = lb
     return o, lse

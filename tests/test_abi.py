@@ -25,7 +25,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
     for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
-                 "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_status_string",
+                 "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
+                 "tg_status_string",
                  "tg_last_error", "tg_abi_version"):
         assert name in syms
 
@@ -84,6 +85,21 @@ def test_attn_rejects_bad_heads_and_head_dim(lib):
     assert lib.tg_gated_attn(tg.TG_BF16, 16, 16, 8, 128, 0.0, *p, FAKE, None, None) == tg.TG_ERR_INVALID_ARG
     assert lib.tg_gated_attn(tg.TG_BF16, 16, 16, 8, 128, 0.1, None, *p[1:], FAKE, None,
                              None) == tg.TG_ERR_INVALID_ARG
+
+
+def test_attn_ex_validation_without_a_gpu(lib):
+    # tg_gated_attn_ex(dtype, cu, batch, max_seqlen, total, hq, hkv, dh, scale, q, k, v, g, head_gain, pos, o,
+    #                  lse, stream); g and head_gain may be NULL, the tensors may not.
+    assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, 0, 16, 8, 128, 0.1, None, None, None, None, None, None,
+                                None, None, None) == tg.TG_OK  # nothing to do
+    assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, 16, 6, 4, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
+                                FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # hq not a multiple of hkv
+    assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, 16, 16, 8, 96, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
+                                FAKE, None, None) == tg.TG_ERR_UNSUPPORTED  # head dim
+    assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, 16, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, None,
+                                FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # NULL pos
+    assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, -1, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
+                                FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # negative total
 
 
 def test_gather_and_rope_validation(lib):

@@ -135,3 +135,52 @@ def test_attn_row_subset_equals_full_rows():
     os_, ls = ref_attn(q, k, v, g, pos, rows=rows)
     np.testing.assert_array_equal(os_, o[rows])
     np.testing.assert_array_equal(ls, lse[:, rows])
+
+
+def _sdpa_causal(q, k, v, hq, hkv):
+    group = hq // hkv
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).permute(1, 0, 2).numpy()
+
+
+def test_attn_without_gate_is_standard_causal_gqa_attention():
+    # Full-context layers: no gate at all is torch's causal attention.
+    q, k, v, _, pos = _rand(11, hq=6, hkv=2)
+    o, _ = ref_attn(q, k, v, None, pos)
+    np.testing.assert_allclose(o, _sdpa_causal(q, k, v, 6, 2), rtol=1e-12, atol=1e-12)
+
+
+def test_attn_zero_head_gain_switches_the_gate_off_per_head():
+    q, k, v, g, pos = _rand(12, hq=4, hkv=2)
+    gain = np.array([0.0, 1.0, 0.0, 1.0])
+    o, lse = ref_attn(q, k, v, g, pos, head_gain=gain)
+    plain = _sdpa_causal(q, k, v, 4, 2)
+    gated, gated_lse = ref_attn(q, k, v, g, pos)
+    for h in (0, 2):
+        np.testing.assert_allclose(o[:, h], plain[:, h], rtol=1e-12, atol=1e-12)
+    for h in (1, 3):
+        np.testing.assert_allclose(o[:, h], gated[:, h], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse[h], gated_lse[h], rtol=1e-13, atol=1e-13)
+
+
+def test_attn_head_gain_two_equals_squared_gate():
+    # gamma * ln g = ln g^gamma: gain 2 on g is gain 1 on g^2 (g^2 stays above FLT_MIN here).
+    q, k, v, g, pos = _rand(13, hq=4, hkv=4)
+    o2, lse2 = ref_attn(q, k, v, g, pos, head_gain=np.full(4, 2.0))
+    osq, lsesq = ref_attn(q, k, v, g * g, pos)
+    np.testing.assert_allclose(o2, osq, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse2, lsesq, rtol=1e-12, atol=1e-12)
+
+
+def test_attn_varlen_passes_gain_and_missing_gate_per_prompt():
+    q, k, v, g, _ = _rand(14, n=30, hq=2, hkv=1)
+    cu = np.array([0, 11, 11, 30])
+    pos = np.concatenate([np.arange(11), np.arange(19)])
+    gain = np.array([0.5, 1.5])
+    o, lse = ref_attn_varlen(q, k, v, None, pos, cu, head_gain=gain)
+    for a, e in ((0, 11), (11, 30)):
+        ob, lb = ref_attn(q[a:e], k[a:e], v[a:e], np.ones(e - a), pos[a:e])
+        np.testing.assert_allclose(o[a:e], ob, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse[:, a:e], lb, rtol=1e-13, atol=1e-13)

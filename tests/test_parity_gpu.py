@@ -330,6 +330,73 @@ def test_attn_bf16_past_the_lds_bias_table(gpu_lib, n, dh):
     assert np.max(np.abs(lse[:, rows] - wl)) <= 1e-3
 
 
+def _gains(hq, seed):
+    gain = np.random.default_rng(seed).uniform(0.0, 2.0, hq).astype(np.float32)
+    gain[0] = 0.0  # one head with the gate switched off
+    return torch.from_numpy(gain)
+
+
+@pytest.mark.parametrize("dtype,n,hq,hkv,dh", [(torch.bfloat16, 300, 16, 8, 128), (torch.bfloat16, 777, 4, 2, 64),
+                                               (torch.float32, 200, 4, 2, 64)])
+def test_attn_head_gain(gpu_lib, dtype, n, hq, hkv, dh):
+    """Per-head gain on the gate bias (tg_gated_attn_ex)."""
+    _say("attn head gain", dtype, n, hq, hkv, dh)
+    q, k, v, g, pos = _attn_inputs(n, hq, hkv, dh, dtype, 41, "wide")
+    gain = _gains(hq, 41)
+    o, lse = gpu_lib.tg_gated_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV), want_lse=True,
+                                   head_gain=gain.to(DEV))
+    torch.cuda.synchronize()
+    wo, wl = ref_attn(q, k, v, g, pos.numpy(), head_gain=gain.numpy())
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == torch.bfloat16 else (1e-4, 1e-4)
+    assert np.max(np.abs(o.cpu().double().numpy() - wo)) <= tol_o
+    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= tol_l
+
+
+def test_attn_head_gain_on_the_streaming_bias_kernel(gpu_lib):
+    n = 8300  # past the LDS bias table at head dim 128
+    q, k, v, g, pos = _attn_inputs(n, 2, 1, 128, torch.bfloat16, 42, "wide")
+    gain = torch.tensor([0.5, 1.75], dtype=torch.float32)
+    o, lse = gpu_lib.tg_gated_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV), want_lse=True,
+                                   head_gain=gain.to(DEV))
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 7, count=48)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy(), rows=rows, head_gain=gain.numpy())
+    assert np.max(np.abs(o.cpu().double().numpy()[rows] - wo)) <= 2e-2
+    assert np.max(np.abs(lse.cpu().double().numpy()[:, rows] - wl)) <= 1e-3
+
+
+@pytest.mark.parametrize("n,dtype", [(300, torch.bfloat16), (32768, torch.bfloat16), (150, torch.float32)])
+def test_attn_without_gate_full_context(gpu_lib, n, dtype):
+    """g=None: plain causal GQA attention, as in the layers at or below the selection layer; at
+    32768 tokens the full-context shape of the 32k workload."""
+    _say("attn no gate", n, dtype)
+    hq, hkv, dh = (16, 8, 128) if dtype == torch.bfloat16 else (4, 2, 64)
+    q, k, v, _, pos = _attn_inputs(n, hq, hkv, dh, dtype, 43, "uniform", pos_kind="dense")
+    o, lse = gpu_lib.tg_gated_attn(q.to(DEV), k.to(DEV), v.to(DEV), None, pos.to(DEV), want_lse=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 8, count=64) if n > 4096 else np.arange(n)
+    wo, wl = ref_attn(q, k, v, None, pos.numpy(), rows=rows)
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == torch.bfloat16 else (1e-4, 1e-4)
+    assert np.max(np.abs(o.cpu().double().numpy()[rows] - wo)) <= tol_o
+    assert np.max(np.abs(lse.cpu().double().numpy()[:, rows] - wl)) <= tol_l
+
+
+def test_attn_varlen_with_head_gain(gpu_lib):
+    lens = [256, 1, 100, 0, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    q, k, v, g, _ = _attn_inputs(total, 4, 2, 128, torch.bfloat16, 44, "wide")
+    pos = torch.from_numpy(np.concatenate([np.arange(m) * 3 for m in lens]).astype(np.int32))
+    gain = _gains(4, 44)
+    o, lse = gpu_lib.tg_gated_attn_varlen(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV),
+                                          torch.from_numpy(cu).to(DEV), max(lens), want_lse=True,
+                                          head_gain=gain.to(DEV))
+    torch.cuda.synchronize()
+    wo, wl = ref_attn_varlen(q, k, v, g, pos.numpy(), cu, head_gain=gain.numpy())
+    assert np.max(np.abs(o.cpu().double().numpy() - wo)) <= 2e-2
+    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= 1e-3
+
+
 def test_attn_varlen_ragged(gpu_lib):
     lens = [256, 1, 100, 256, 129, 0, 256]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
