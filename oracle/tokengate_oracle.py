@@ -38,6 +38,7 @@ __all__ = [
     "ref_rope_kv",
     "ref_attn",
     "ref_attn_varlen",
+    "ref_decode",
 ]
 
 
@@ -266,4 +267,46 @@ def ref_attn_varlen(q, k, v, g, pos, cu_seqlens, scale: float | None = None, hea
                           head_gain=head_gain)
         o[a:e] = ob
         lse[:, a:e] = lb
+    return o, lse
+
+
+def ref_decode(q, k_cache, v_cache, g, cu_seqlens, scale: float | None = None, head_gain=None):
+    """One new query per sequence over its whole cache (no causal mask: every
+    cached key precedes the new token).
+
+    q [B, hq, dh]; k_cache, v_cache [total, hkv, dh] packed by ``cu_seqlens``
+    [B + 1]; g [total] or None.  Returns (o [B, hq, dh], lse [B, hq]) float64;
+    a sequence with an empty cache gives o = 0 and lse = -inf.
+
+    READING (decode is not described on the pages): the compact cache keeps
+    the kept prompt tokens' gate bias ln max(g_j, FLT_MIN) (times the head's
+    gain), exactly as in the gated prefill attention; generated tokens carry
+    g = 1 (bias 0), and g=None means no bias at all.
+    """
+    q = _f64(q)
+    kc = _f64(k_cache)
+    vc = _f64(v_cache)
+    cu = _i64(cu_seqlens)
+    B, hq, dh = q.shape
+    hkv = kc.shape[1]
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    gain = np.ones(hq) if head_gain is None else _f64(head_gain)
+    bias_all = None if g is None else np.log(np.maximum(_f64(g), FLT_MIN))
+    o = np.zeros((B, hq, dh))
+    lse = np.full((B, hq), -np.inf)
+    for b in range(B):
+        a, e = cu[b], cu[b + 1]
+        if e == a:
+            continue
+        bias = np.zeros(e - a) if bias_all is None else bias_all[a:e]
+        for h in range(hq):
+            kvh = h // group
+            s = scale * (kc[a:e, kvh, :] @ q[b, h, :]) + gain[h] * bias
+            m = s.max()
+            p = np.exp(s - m)
+            l = p.sum()
+            o[b, h, :] = (p @ vc[a:e, kvh, :]) / l
+            lse[b, h] = m + np.log(l)
     return o, lse
