@@ -258,6 +258,49 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
                                   const void* v, const float* g, const float* head_gain,
                                   const int32_t* pos, void* o, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Decode attention over the compact KV cache.  [aitu] section 3: past the
+ * selection layer only the kept tokens have keys and values, so each newly
+ * generated token attends over its sequence's compact cache.  Decode itself
+ * is not described on the pages; this library's reading: the kept prompt
+ * keys keep their gate bias, tokens appended while generating carry g = 1
+ * (bias 0), and every cached key precedes the new token (no mask).  For
+ * sequence b and query head h (KV head h / (hq/hkv)):
+ *   o[b,h]   = sum_j softmax_j(scale * q[b,h].k_j + gamma_h ln max(g_j, FLT_MIN)) v_j
+ *   lse[b,h] = ln sum_j exp(scale * q[b,h].k_j + gamma_h ln max(g_j, FLT_MIN))
+ * over j in [cu_seqlens[b], cu_seqlens[b+1]).  An empty cache gives o = 0
+ * and lse = -inf.
+ *
+ *   dtype       TG_BF16: bf16 q/caches/o, fp32 products and softmax.
+ *               TG_FP32: fp32 throughout.
+ *   cu_seqlens  [batch + 1] int32 (device), non-decreasing, cu_seqlens[0] = 0;
+ *               cache lengths must not exceed max_seqlen (host).  Not checked.
+ *   hq, hkv     heads; hq / hkv in {1, 2, 4, 8}.   dh: 64 or 128.
+ *   scale       logit scale, > 0.
+ *   q           [batch, hq, dh] (rotated) new-token queries.
+ *   k_cache,
+ *   v_cache     [cu_seqlens[batch], hkv, dh] packed caches (rotated keys).
+ *   g           [cu_seqlens[batch]] fp32 gate values, or NULL for no bias.
+ *   head_gain   [hq] fp32 gamma_h, or NULL for 1.
+ *   o           [batch, hq, dh] output, dtype.   lse: [batch, hq] fp32 or NULL.
+ *   workspace   device memory owned by the caller, 16-byte aligned, at least
+ *               tg_decode_attn_workspace_size(...) bytes: partial results of
+ *               the key blocks; contents need not be initialised and are
+ *               left undefined.  Calls that share a workspace must not
+ *               overlap.  The library allocates nothing.
+ * Errors: TG_ERR_INVALID_ARG for NULL pointers, misalignment, a too-small
+ * workspace or out-of-range sizes; TG_ERR_UNSUPPORTED for other head ratios
+ * or dh; TG_ERR_HIP for a failed launch.  batch = 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+TG_API int64_t tg_decode_attn_workspace_size(int32_t batch, int64_t max_seqlen, int32_t hq,
+                                             int32_t hkv, int32_t dh);
+TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh,
+                                float scale, const void* q, const void* k_cache,
+                                const void* v_cache, const float* g, const float* head_gain,
+                                void* o, float* lse, void* workspace, int64_t workspace_bytes,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

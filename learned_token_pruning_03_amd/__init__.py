@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     TokenGateError,
     load_library,
     status_string,
+    tg_decode_attn,
+    tg_decode_attn_workspace_size,
     tg_gate_score,
     tg_gated_attn,
     tg_gated_attn_varlen,

@@ -50,6 +50,9 @@ SIGNATURES = {
                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_gated_attn_ex": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp,
                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_decode_attn_workspace_size": ([_c_i32, _c_i64, _c_i32, _c_i32, _c_i32], _c_i64),
+    "tg_decode_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
+                        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -283,4 +286,39 @@ def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: O
                lib.tg_gated_attn_varlen(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv,
                                         dh, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(pos), _ptr(o),
                                         _ptr(lse), _stream(q)))
+    return (o, lse) if (want_lse or lse is not None) else o
+
+
+def tg_decode_attn_workspace_size(batch: int, max_seqlen: int, hq: int, hkv: int, dh: int) -> int:
+    n = load_library().tg_decode_attn_workspace_size(batch, int(max_seqlen), hq, hkv, dh)
+    _need(n >= 0, "invalid decode sizes")
+    return n
+
+
+def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, g: Optional[torch.Tensor],
+                   cu_seqlens: torch.Tensor, max_seqlen: int, scale: Optional[float] = None,
+                   head_gain: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                   workspace: Optional[torch.Tensor] = None):
+    """One new query per sequence over its packed cache; q [B, hq, dh]."""
+    lib = load_library()
+    batch, hq, dh = q.shape
+    hkv = k_cache.shape[1]
+    _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.numel() == batch + 1, "cu_seqlens is int32 [B + 1]")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and the caches share a dtype")
+    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
+          "head_gain is fp32 [hq]")
+    if scale is None:
+        scale = dh ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(batch, hq, dtype=torch.float32, device=q.device)
+    need = tg_decode_attn_workspace_size(batch, max_seqlen, hq, hkv, dh)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("tg_decode_attn",
+           lib.tg_decode_attn(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), hq, hkv, dh, float(scale),
+                              _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(g), _ptr(head_gain), _ptr(o), _ptr(lse),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o

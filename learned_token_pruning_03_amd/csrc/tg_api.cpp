@@ -278,4 +278,50 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
                   "attn_ex");
 }
 
+// ---------------------------------------------------------------------------
+static int64_t decode_ws_bytes(int32_t batch, int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh) {
+  if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32 || hq <= 0 || hkv <= 0 || hq % hkv != 0 ||
+      (dh != 64 && dh != 128))
+    return -1;
+  const int split = tg::decode_split_keys(batch, hkv, max_seqlen);
+  int64_t nsplit = (max_seqlen + split - 1) / split;
+  if (nsplit < 1) nsplit = 1;
+  return (int64_t)batch * hq * nsplit * (dh + 2) * (int64_t)sizeof(float);
+}
+
+TG_API int64_t tg_decode_attn_workspace_size(int32_t batch, int64_t max_seqlen, int32_t hq, int32_t hkv,
+                                             int32_t dh) {
+  return decode_ws_bytes(batch, max_seqlen, hq, hkv, dh);
+}
+
+TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
+                                const void* q, const void* k_cache, const void* v_cache, const float* g,
+                                const float* head_gain, void* o, float* lse, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "decode: unknown dtype %d", (int)dtype);
+  if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "decode: batch or max_seqlen out of range");
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(TG_ERR_INVALID_ARG, "decode: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  const int group = hq / hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(TG_ERR_UNSUPPORTED, "decode: hq/hkv=%d must be 1, 2, 4 or 8", group);
+  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "decode: dh=%d must be 64 or 128", dh);
+  if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "decode: scale must be > 0");
+  if (batch == 0) return ok();
+  if (!cu_seqlens || !q || !k_cache || !v_cache || !o || !workspace)
+    return fail(TG_ERR_INVALID_ARG, "decode: NULL pointer argument");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return fail(TG_ERR_INVALID_ARG, "decode: q, k_cache, v_cache and workspace must be 16-byte aligned");
+  const int64_t need = decode_ws_bytes(batch, max_seqlen, hq, hkv, dh);
+  if (workspace_bytes < need)
+    return fail(TG_ERR_INVALID_ARG, "decode: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  return from_hip(tg::launch_decode(elem_size(dtype), cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q,
+                                    k_cache, v_cache, g, head_gain, o, lse, static_cast<float*>(workspace),
+                                    stream),
+                  "decode");
+}
+
 }  // extern "C"

@@ -107,4 +107,12 @@ hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
                            const float* head_gain, const int32_t* pos, float* o, float* lse,
                            hipStream_t stream);
 
+// Decode attention: keys per split-K block, and the launch of the split and
+// combine kernels (workspace: batch * hq * nsplit * (dh + 2) floats).
+int decode_split_keys(int64_t batch, int hkv, int64_t max_seqlen);
+hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, int64_t max_seqlen, int hq,
+                         int hkv, int dh, float scale, const void* q, const void* k, const void* v,
+                         const float* g, const float* head_gain, void* o, float* lse, float* workspace,
+                         hipStream_t stream);
+
 }  // namespace tg

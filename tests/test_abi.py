@@ -26,6 +26,7 @@ def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
     for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
+                 "tg_decode_attn_workspace_size", "tg_decode_attn",
                  "tg_status_string",
                  "tg_last_error", "tg_abi_version"):
         assert name in syms
@@ -100,6 +101,33 @@ def test_attn_ex_validation_without_a_gpu(lib):
                                 FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # NULL pos
     assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, -1, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
                                 FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # negative total
+
+
+def test_decode_validation_without_a_gpu(lib):
+    # tg_decode_attn(dtype, cu, batch, max_seqlen, hq, hkv, dh, scale, q, k_cache, v_cache, g, head_gain, o, lse,
+    #                workspace, workspace_bytes, stream)
+    ws = lib.tg_decode_attn_workspace_size(4, 5000, 16, 8, 128)
+    assert ws > 0 and ws % 16 == 0
+    assert lib.tg_decode_attn_workspace_size(4, 5000, 16, 8, 96) == -1
+    assert lib.tg_decode_attn_workspace_size(4, 5000, 6, 4, 128) == -1
+    assert lib.tg_decode_attn_workspace_size(-1, 5000, 16, 8, 128) == -1
+    assert lib.tg_decode_attn_workspace_size(4, 0, 16, 8, 128) > 0  # empty caches still write o and lse
+
+    def call(batch=4, max_seqlen=5000, hq=16, hkv=8, dh=128, scale=0.1, q=FAKE, ws_bytes=ws, cu=FAKE):
+        return lib.tg_decode_attn(tg.TG_BF16, cu, batch, max_seqlen, hq, hkv, dh, scale, q, FAKE, FAKE, None,
+                                  None, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(batch=0) == tg.TG_OK  # nothing to do
+    assert call(hq=24, hkv=8) == tg.TG_ERR_UNSUPPORTED  # three query heads per KV head
+    assert call(hq=32, hkv=2) == tg.TG_ERR_UNSUPPORTED  # sixteen
+    assert call(dh=96) == tg.TG_ERR_UNSUPPORTED
+    assert call(hq=6, hkv=4) == tg.TG_ERR_INVALID_ARG
+    assert call(scale=0.0) == tg.TG_ERR_INVALID_ARG
+    assert call(q=None) == tg.TG_ERR_INVALID_ARG
+    assert call(cu=None) == tg.TG_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 4) == tg.TG_ERR_INVALID_ARG
+    assert b"workspace" in lib.tg_last_error()
+    assert call(max_seqlen=-1) == tg.TG_ERR_INVALID_ARG
 
 
 def test_gather_and_rope_validation(lib):

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import learned_token_pruning_03_amd.workloads as W
-from oracle import ref_attn, ref_attn_varlen, ref_gate, ref_gather, ref_rope, ref_select, ref_select_varlen
+from oracle import ref_attn, ref_attn_varlen, ref_decode, ref_gate, ref_gather, ref_rope, ref_select, ref_select_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -475,3 +475,81 @@ def test_repeat_runs_are_bitwise_identical(gpu_lib):
             first = cur
         else:
             assert torch.equal(cur[0], first[0]) and torch.equal(cur[1].view(torch.int16), first[1].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- decode
+def _decode_case(tg, lens, hq, hkv, dh, dtype, seed, gkind="uniform", gain=False):
+    B, total = len(lens), int(sum(lens))
+    q, _, _ = W.qkv(B, hq, hkv, dh, 1.0 / dh, dtype, seed)
+    _, k, v = W.qkv(total, hq, hkv, dh, 1.0 / dh, dtype, seed + 1)
+    g = None
+    if gkind == "uniform":
+        g = W.random_scores(total, seed)
+    elif gkind == "wide":
+        g = W.gate_values_wide(total, seed)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    hg = _gains(hq, seed) if gain else None
+    o_ref, lse_ref = ref_decode(q, k, v, g, cu, head_gain=hg)
+    o, lse = tg.tg_decode_attn(q.to(DEV), k.to(DEV), v.to(DEV), None if g is None else g.to(DEV), cu.to(DEV),
+                               max(lens), head_gain=None if hg is None else hg.to(DEV), want_lse=True)
+    torch.cuda.synchronize()
+    return o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref
+
+
+@pytest.mark.parametrize("dtype,lens,hq,hkv,dh,gkind,gain", [
+    (torch.bfloat16, [0, 1, 37, 1000, 4099], 16, 8, 128, "uniform", True),
+    (torch.bfloat16, [513, 2048, 64], 32, 4, 64, "wide", False),
+    (torch.bfloat16, [300, 7], 4, 2, 128, None, False),
+    (torch.bfloat16, [4096 + 37] * 3, 16, 16, 64, "uniform", True),
+    (torch.float32, [5, 300, 1025], 4, 4, 128, None, False),
+    (torch.float32, [0, 2, 777], 8, 2, 64, "wide", True),
+])
+def test_decode_parity(gpu_lib, dtype, lens, hq, hkv, dh, gkind, gain):
+    _say("decode", dtype, lens, hq, hkv, dh, gkind, gain)
+    o, lse, o_ref, lse_ref = _decode_case(gpu_lib, lens, hq, hkv, dh, dtype, 31 + sum(lens), gkind, gain)
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == torch.bfloat16 else (1e-4, 1e-4)
+    err_o = float(np.max(np.abs(o - o_ref)))
+    live = np.isfinite(lse_ref)
+    err_l = float(np.max(np.abs(lse[live] - lse_ref[live])))
+    _say("  max abs err o", err_o, "lse", err_l)
+    assert err_o <= tol_o and err_l <= tol_l
+    assert np.array_equal(np.isfinite(lse), live)  # empty caches: lse = -inf
+    assert np.all(o[~live] == 0.0)
+
+
+def test_decode_bench_shape_sampled(gpu_lib):
+    # 32 sequences with 4096-key compact caches (the 32k prompt's budget) plus
+    # a few generated tokens each; the oracle checks a sample of sequences.
+    rng = np.random.default_rng(5)
+    lens = [4096 + int(x) for x in rng.integers(0, 256, 32)]
+    hq, hkv, dh = 16, 8, 128
+    q, _, _ = W.qkv(32, hq, hkv, dh, 1.0 / dh, torch.bfloat16, 77)
+    _, k, v = W.qkv(sum(lens), hq, hkv, dh, 1.0 / dh, torch.bfloat16, 78)
+    g = W.random_scores(sum(lens), 79)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    o, lse = gpu_lib.tg_decode_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), cu.to(DEV), max(lens),
+                                    want_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    for b in (0, 13, 31):
+        a, e = int(cu[b]), int(cu[b + 1])
+        o_ref, lse_ref = ref_decode(q[b:b + 1], k[a:e], v[a:e], g[a:e], np.array([0, e - a]))
+        assert np.max(np.abs(o[b] - o_ref[0])) <= 2e-2
+        assert np.max(np.abs(lse[b] - lse_ref[0])) <= 1e-3
+
+
+def test_decode_reuses_a_dirty_workspace(gpu_lib):
+    # The workspace needs no clearing: a second call over the same (dirty)
+    # buffer with other lengths gives the oracle's result.
+    hq, hkv, dh = 16, 8, 128
+    ws = torch.full((gpu_lib.tg_decode_attn_workspace_size(3, 5000, hq, hkv, dh),), 255, dtype=torch.uint8,
+                    device=DEV)
+    for lens in ([5000, 4000, 1], [17, 0, 2500]):
+        q, _, _ = W.qkv(3, hq, hkv, dh, 1.0 / dh, torch.bfloat16, 90 + lens[0])
+        _, k, v = W.qkv(sum(lens), hq, hkv, dh, 1.0 / dh, torch.bfloat16, 91 + lens[0])
+        g = W.random_scores(sum(lens), 92)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+        o = gpu_lib.tg_decode_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), cu.to(DEV), 5000, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, _ = ref_decode(q, k, v, g, cu)
+        assert np.max(np.abs(o.cpu().double().numpy() - o_ref)) <= 2e-2
