@@ -42,6 +42,8 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-full-context", action="store_true",
                    help="skip the comparison with one ungated layer over all N tokens")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode attention figure over compact KV caches")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the run, launch a plain 1 GiB -> 1 GiB streaming kernel (torch.neg on fp32) "
@@ -204,6 +206,46 @@ def full_context(tg, W, sh, dev, reps=8):
     a = statistics.median(attn_t)
     return {"n": sh.n, "rope_kv_us": round(statistics.median(rope_t), 2), "attn_us": round(a, 2),
             "attn_TFLOP/s": round(flops / (a * 1e-6) / 1e12, 1)}
+
+
+def decode_step(tg, W, sh, dev, batch=32, reps=20):
+    """Decode attention of one upper layer after pruning: `batch` sequences,
+    each one new query over its compact cache of K kept prompt tokens plus a
+    ragged 0-255 generated tokens (gate 1), median of event-timed launches.
+    Algorithmic bytes: the caches (K and V), the gate values, q and o."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(11)
+    lens = [sh.k + int(x) for x in rng.integers(0, 256, batch)]
+    total = int(sum(lens))
+    q, _, _ = W.qkv(batch, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 12)
+    _, kc, vc = W.qkv(total, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 13)
+    g = torch.ones(total)
+    for b in range(batch):  # the kept prompt tokens carry their gate values
+        a = sum(lens[:b])
+        g[a:a + sh.k] = W.random_scores(sh.k, 14 + b)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    q, kc, vc, g, cu = (t.to(dev) for t in (q, kc, vc, g, cu))
+    o = torch.empty_like(q)
+    lse = torch.empty(batch, sh.hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(tg.tg_decode_attn_workspace_size(batch, max(lens), sh.hq, sh.hkv, sh.dh), dtype=torch.uint8,
+                     device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for r in range(reps + 2):
+        ev[0].record()
+        tg.tg_decode_attn(q, kc, vc, g, cu, max(lens), o=o, lse=lse, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    esz = 2 if sh.dtype == torch.bfloat16 else 4
+    byts = 2 * total * sh.hkv * sh.dh * esz + 4 * total + 2 * batch * sh.hq * sh.dh * esz + 4 * batch * sh.hq
+    us = statistics.median(ts)
+    return {"batch": batch, "cache_len_mean": round(total / batch, 1), "us": round(us, 2),
+            "GB/s": round(byts / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "tokens/s": round(batch / (us * 1e-6), 1)}
 
 
 def cpu_baseline(W, name):
@@ -423,6 +465,11 @@ def main(argv=None):
         # prompt; every upper layer then runs on K tokens instead of N.
         full["pruning_overhead_us"] = round(med["gate"] + med["select"] + med["gather"], 2)
 
+    dec = None
+    if not args.no_decode:
+        print("[bench] timing decode attention over compact caches ...", file=sys.stderr, flush=True)
+        dec = decode_step(tg, W, sh, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
@@ -448,6 +495,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "stages": stages,
         "full_context": full,
+        "decode": dec,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "gate_pct_hbm_peak": round(100 * by["gate"] / (med["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "gather_pct_hbm_peak": round(100 * by["gather"] / (med["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),

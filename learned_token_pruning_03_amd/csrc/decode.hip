@@ -41,28 +41,51 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
 
+// Raw 8-element chunk of a row: one 16-byte load for bf16, two for fp32.
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* x);
-
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* x) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+struct Raw8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void to_f32(float* x) const {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
   }
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void to_f32(float* x) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+};
+
+// DPP lane moves within a row of 16 lanes (quad permutations and mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* x) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
+// Sum over each aligned group of N lanes (N = 8 or 16), result in every lane.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp<0x141>(x);  // row_half_mirror: the other quad of each 8 lanes
+  if constexpr (N == 16) x += dpp<0x140>(x);  // row_mirror: the other half of the row
+  return x;
 }
 
 struct DecArgs {
@@ -72,7 +95,8 @@ struct DecArgs {
   const float* g;
   const float* head_gain;
   const int32_t* cu;
-  float* part;  // [batch, hq, nsplit, DH + 2]: m (log2 units), l, o[DH] (not normalised)
+  float* part_o;   // [batch, hq, nsplit, DH]: block outputs, not normalised
+  float* part_ml;  // [batch, hq, nsplit, 2]: block maximum (log2 units) and sum
   void* o;
   float* lse;
   int hq;
@@ -83,8 +107,9 @@ struct DecArgs {
 };
 
 // GROUP = query heads per KV head (compile-time so that per-head state stays
-// in registers).
-template <typename T, int DH, int GROUP>
+// in registers).  U = steps (of KPB keys) per loop iteration; the loads of
+// the next iteration are in flight while the current one is computed.
+template <typename T, int DH, int GROUP, int U>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
   constexpr int LPK = DH / 8;          // lanes per key row
   constexpr int KPW = kWave / LPK;     // key rows per wave per step
@@ -104,11 +129,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
   const int k1 = min(L, k0 + a.split);
   const float c = a.scale_log2;
 
+  const T* kb = reinterpret_cast<const T*>(a.k) + (s0 * a.hkv + kvh) * DH + dc * 8;
+  const T* vb = reinterpret_cast<const T*>(a.v) + (s0 * a.hkv + kvh) * DH + dc * 8;
+  // Gate values; with no gate the loads read a valid dummy word (cu) and the
+  // value is replaced by 1, so that no load sits in a branch.
+  const bool has_g = a.g != nullptr;
+  const float* gb = has_g ? a.g + s0 : reinterpret_cast<const float*>(a.cu);
+  const int64_t row = (int64_t)a.hkv * DH;  // elements between consecutive keys
+  const int my = wave * KPW + ks;           // this lane's key within a step
+
+  Raw8<T> rk[U], rv[U];
+  float rg[U];
+  auto issue = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jr = min(j0 + u * KPB + my, k1 - 1);  // past the block: reload its last row
+      rk[u].load(kb + jr * row);
+      rv[u].load(vb + jr * row);
+      const float gl = gb[has_g ? jr : 0];
+      rg[u] = has_g ? gl : 1.0f;
+    }
+  };
+  issue(k0);
+
   float qv[GROUP][8], gain[GROUP];
 #pragma unroll
   for (int i = 0; i < GROUP; ++i) {
     const int h = kvh * GROUP + i;
-    load8<T>(reinterpret_cast<const T*>(a.q) + ((int64_t)b * a.hq + h) * DH + dc * 8, qv[i]);
+    Raw8<T> rq;
+    rq.load(reinterpret_cast<const T*>(a.q) + ((int64_t)b * a.hq + h) * DH + dc * 8);
+    rq.to_f32(qv[i]);
     gain[i] = a.head_gain ? a.head_gain[h] : 1.0f;
   }
   float m[GROUP], l[GROUP], acc[GROUP][8];
@@ -120,33 +170,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
   }
 
-  const T* kb = reinterpret_cast<const T*>(a.k) + (s0 * a.hkv + kvh) * DH + dc * 8;
-  const T* vb = reinterpret_cast<const T*>(a.v) + (s0 * a.hkv + kvh) * DH + dc * 8;
-  const int64_t row = (int64_t)a.hkv * DH;  // elements between consecutive keys
-  // Two steps per iteration, loads first, so that four 16-byte loads per lane
-  // are in flight.
-  for (int j0 = k0; j0 < k1; j0 += 2 * KPB) {
-    float kx[2][8], vx[2][8];
-    int jj[2];
+  for (int j0 = k0; j0 < k1; j0 += U * KPB) {
+    float kx[U][8], vx[U][8], bias[U];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      jj[u] = j0 + u * KPB + wave * KPW + ks;
-      const int jr = jj[u] < k1 ? jj[u] : k1 - 1;
-      load8<T>(kb + jr * row, kx[u]);
-      load8<T>(vb + jr * row, vx[u]);
+    for (int u = 0; u < U; ++u) {
+      rk[u].to_f32(kx[u]);
+      rv[u].to_f32(vx[u]);
+      bias[u] = log2f(fmaxf(rg[u], kFltMin));  // g = 1 (no gate) gives 0
     }
+    if (j0 + U * KPB < k1) issue(j0 + U * KPB);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float bias = a.g ? log2f(fmaxf(a.g[s0 + (jj[u] < k1 ? jj[u] : k1 - 1)], kFltMin)) : 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const bool live = j0 + u * KPB + my < k1;
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
         float d = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = fmaf(qv[i][e], kx[u][e], d);
-#pragma unroll
-        for (int o = LPK / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, kWave);
+        d = group_sum<LPK>(d);
         // Logit in log2 units; rows past this block weigh nothing.
-        const float t = jj[u] < k1 ? fmaf(d, c, gain[i] * bias) : -INFINITY;
+        const float t = live ? fmaf(d, c, gain[i] * bias[u]) : -INFINITY;
         if (t > m[i] + 8.0f) {
           const float alpha = m[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[i] - t);
           l[i] *= alpha;
@@ -187,16 +230,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  // Merge the waves; thread t < GROUP*DH owns (head t / DH, dimension t % DH).
+  // Merge the waves: thread t handles (head t / (DH + 2), entry t % (DH + 2)),
+  // entries DH and DH + 1 being the maximum and the sum.
   for (int t = tid; t < GROUP * (DH + 2); t += kDecThreads) {
     const int i = t / (DH + 2), d = t % (DH + 2);
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, red[w][i][DH]);
-    float val = 0.0f;
-    if (d == DH) {
-      val = mx;
-    } else {
+    float val = mx;
+    if (d != DH) {
+      val = 0.0f;
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) {
         const float mw = red[w][i][DH];
@@ -204,32 +247,74 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
         val += red[w][i][d] * f;
       }
     }
-    const int h = kvh * GROUP + i;
-    a.part[(((int64_t)b * a.hq + h) * a.nsplit + split) * (DH + 2) + d] = val;
+    const int64_t slot = ((int64_t)b * a.hq + kvh * GROUP + i) * a.nsplit + split;
+    if (d < DH)
+      a.part_o[slot * DH + d] = val;
+    else
+      a.part_ml[slot * 2 + (d - DH)] = val;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float block_reduce(float x, bool is_max, float* scratch) {
+  // N threads (64 or 128); scratch holds N / 64 floats.
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float y = __shfl_xor(x, o, kWave);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  if constexpr (N == 64) {
+    return x;
+  } else {
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+    __syncthreads();
+    return is_max ? fmaxf(scratch[0], scratch[1]) : scratch[0] + scratch[1];
   }
 }
 
 template <typename T, int DH>
 __global__ __launch_bounds__(DH) void decode_combine_kernel(DecArgs a) {
+  constexpr int CH = 512;  // block weights staged in LDS per chunk
+  __shared__ float wts[CH];
+  __shared__ float scr[2];
   const int d = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = a.cu[b + 1] - a.cu[b];
   const int ns = min(a.nsplit, (L + a.split - 1) / a.split);  // blocks that ran for this sequence
-  const float* p = a.part + ((int64_t)b * a.hq + h) * a.nsplit * (DH + 2);
+  const int64_t base = ((int64_t)b * a.hq + h) * a.nsplit;
+  const float* po = a.part_o + base * DH;
+  const float* pml = a.part_ml + base * 2;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, p[s * (DH + 2) + DH]);
+  for (int s = d; s < ns; s += DH) mx = fmaxf(mx, pml[2 * s]);
+  mx = block_reduce<DH>(mx, true, scr);
   float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = p[s * (DH + 2) + DH];
-    const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
-    num = fmaf(p[s * (DH + 2) + d], f, num);
-    den = fmaf(p[s * (DH + 2) + DH + 1], f, den);
+  for (int c0 = 0; c0 < ns; c0 += CH) {
+    const int n = min(CH, ns - c0);
+    __syncthreads();
+    for (int s = d; s < n; s += DH) {
+      const float ms = pml[2 * (c0 + s)];
+      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
+      wts[s] = w;
+      den = fmaf(w, pml[2 * (c0 + s) + 1], den);
+    }
+    __syncthreads();
+    const float* pc = po + (int64_t)c0 * DH + d;
+    int s = 0;
+    for (; s + 8 <= n; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = pc[(s + e) * DH];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num = fmaf(wts[s + e], x[e], num);
+    }
+    for (; s < n; ++s) num = fmaf(wts[s], pc[s * DH], num);
   }
+  den = block_reduce<DH>(den, false, scr);
   const float ov = den > 0.0f ? num / den : 0.0f;  // empty cache: zeros
   const int64_t oi = ((int64_t)b * a.hq + h) * DH + d;
   if constexpr (sizeof(T) == 2) {
-    __bf16 hv = (__bf16)ov;
-    reinterpret_cast<__bf16*>(a.o)[oi] = hv;
+    reinterpret_cast<__bf16*>(a.o)[oi] = (__bf16)ov;
   } else {
     reinterpret_cast<float*>(a.o)[oi] = ov;
   }
@@ -238,7 +323,7 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(DecArgs a) {
 
 template <typename T, int DH, int GROUP>
 void launch_group(const DecArgs& a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, DH, GROUP>), dim3(a.nsplit, a.hkv, batch), dim3(kDecThreads), 0,
+  hipLaunchKernelGGL((decode_split_kernel<T, DH, GROUP, 2>), dim3(a.nsplit, a.hkv, batch), dim3(kDecThreads), 0,
                      stream, a);
   hipLaunchKernelGGL((decode_combine_kernel<T, DH>), dim3(a.hq, batch), dim3(DH), 0, stream, a);
 }
@@ -268,7 +353,7 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
   a.g = g;
   a.head_gain = head_gain;
   a.cu = cu_seqlens;
-  a.part = workspace;
+  a.part_o = workspace;
   a.o = o;
   a.lse = lse;
   a.hq = hq;
@@ -276,6 +361,7 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
   a.split = decode_split_keys(batch, hkv, max_seqlen);
   a.nsplit = (int)((max_seqlen + a.split - 1) / a.split);
   if (a.nsplit < 1) a.nsplit = 1;
+  a.part_ml = workspace + (int64_t)batch * hq * a.nsplit * dh;
   a.scale_log2 = scale * kLog2e;
   if (elem_bytes == 2)
     return dh == 128 ? launch_dh<uint16_t, 128>(a, batch, stream) : launch_dh<uint16_t, 64>(a, batch, stream);
