@@ -39,6 +39,9 @@ __all__ = [
     "ref_attn",
     "ref_attn_varlen",
     "ref_decode",
+    "ref_linear",
+    "ref_swiglu",
+    "ref_mlp",
 ]
 
 
@@ -310,3 +313,39 @@ def ref_decode(q, k_cache, v_cache, g, cu_seqlens, scale: float | None = None, h
             o[b, h, :] = (p @ vc[a:e, kvh, :]) / l
             lse[b, h] = m + np.log(l)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Upper-layer dense work on the kept tokens.
+#
+# [aitualizate] section 3: every layer above the selection layer processes only
+# the kept tokens, so its projections and MLP run on K rows instead of N.  The
+# layer shape is the base model the pages evaluate (the paper page's setup
+# table: Qwen3-1.7B in bf16): QKV and O projections without bias and a SwiGLU
+# MLP.  READING: the LoRA adapters of that setup (rank 16, alpha 32, on the
+# query and value projections) are merged into the weights before the path,
+# W' = W + (alpha / r) B A, so each projection is one plain product with W'.
+
+
+def ref_linear(x, w, residual=None):
+    """y = x W^T (+ residual): x [M, Kin], w [Nout, Kin] (nn.Linear layout),
+    residual [M, Nout] or None.  float64."""
+    y = _f64(x) @ _f64(w).T
+    if residual is not None:
+        y = y + _f64(residual)
+    return y
+
+
+def _silu(z: np.ndarray) -> np.ndarray:
+    return z * _sigmoid(z)
+
+
+def ref_swiglu(x, w_gate, w_up):
+    """SwiGLU hidden activation: SiLU(x W_gate^T) * (x W_up^T), with
+    w_gate, w_up [F, Kin].  Returns [M, F] float64."""
+    return _silu(ref_linear(x, w_gate)) * ref_linear(x, w_up)
+
+
+def ref_mlp(x, w_gate, w_up, w_down, residual=None):
+    """The MLP block: SwiGLU(x) W_down^T (+ residual), w_down [d, F]."""
+    return ref_linear(ref_swiglu(x, w_gate, w_up), w_down, residual)
