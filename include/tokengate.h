@@ -301,6 +301,44 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
                                 void* o, float* lse, void* workspace, int64_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Upper-layer dense work on the kept tokens.  [aitu] section 3: every layer
+ * above the selection layer processes only the kept tokens, so its
+ * projections and MLP are products of the [K, d] kept activations with the
+ * layer's weights.  Layer shape: the base model of the [paper] setup table
+ * (Qwen3-1.7B, bf16): bias-free QKV / O projections and a SwiGLU MLP.  The
+ * setup's LoRA adapters (rank 16, alpha 32, query and value projections) are
+ * taken as merged into W before the path (W + (alpha/r) B A).
+ *
+ * tg_linear:  y = x W^T            (residual NULL)
+ *             y = x W^T + residual  (residual may equal y: in-place add)
+ * tg_swiglu:  y = SiLU(x Wg^T) * (x Wu^T),  SiLU(z) = z / (1 + e^-z)
+ * The MLP block is tg_swiglu followed by tg_linear with W_down and the
+ * residual stream.
+ *
+ *   dtype     TG_BF16 only (TG_FP32 gives TG_ERR_UNSUPPORTED): bf16 operands,
+ *             fp32 accumulation (MFMA), one bf16 rounding of the result (after
+ *             the residual add / the SwiGLU product).
+ *   m         rows (tokens), 0 <= m < 2^31 (0 is a no-op).
+ *   n         output columns of tg_linear, a multiple of 256.
+ *   f         output columns of tg_swiglu, a multiple of 128.
+ *   k         inner size, a multiple of 32.
+ *   x         [m, ld_x] bf16, row-major, 16-byte aligned, ld_x >= k, ld_x % 8 == 0.
+ *   w         [n, ld_w] bf16 (nn.Linear layout: one output per row),
+ *             16-byte aligned, ld_w >= k, ld_w % 8 == 0.  w_gate, w_up: [f, ld_w].
+ *   residual  [m, ld_r] bf16 or NULL.
+ *   y         [m, ld_y] bf16, ld_y >= n (or f).  Must not overlap x or w.
+ * Errors: TG_ERR_INVALID_ARG for NULL pointers, misalignment, bad leading
+ * dimensions or sizes out of range; TG_ERR_UNSUPPORTED for other dtypes and
+ * for n, f, k off the multiples above; TG_ERR_HIP for a failed launch.
+ * ------------------------------------------------------------------------- */
+TG_API tg_status tg_linear(tg_dtype dtype, int64_t m, int32_t n, int32_t k, const void* x,
+                           int64_t ld_x, const void* w, int64_t ld_w, const void* residual,
+                           int64_t ld_r, void* y, int64_t ld_y, hipStream_t stream);
+TG_API tg_status tg_swiglu(tg_dtype dtype, int64_t m, int32_t f, int32_t k, const void* x,
+                           int64_t ld_x, const void* w_gate, const void* w_up, int64_t ld_w,
+                           void* y, int64_t ld_y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

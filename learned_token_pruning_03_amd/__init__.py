@@ -24,8 +24,10 @@ from .binding import (  # noqa: F401
     tg_gated_attn_varlen,
     tg_gather,
     tg_gather_varlen,
+    tg_linear,
     tg_rope_kv,
     tg_rope_table,
     tg_select_topk,
     tg_select_topk_varlen,
+    tg_swiglu,
 )

@@ -50,6 +50,10 @@ SIGNATURES = {
                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_gated_attn_ex": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp,
                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_linear": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64,
+                   _c_vp], ctypes.c_int),
+    "tg_swiglu": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+                  ctypes.c_int),
     "tg_decode_attn_workspace_size": ([_c_i32, _c_i64, _c_i32, _c_i32, _c_i32], _c_i64),
     "tg_decode_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
@@ -322,3 +326,34 @@ def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                               _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(g), _ptr(head_gain), _ptr(o), _ptr(lse),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o
+
+
+def tg_linear(x: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None,
+              y: Optional[torch.Tensor] = None):
+    """y = x W^T (+ residual); x [M, K], w [N, K] (row strides taken from the tensors)."""
+    lib = load_library()
+    m, k = x.shape
+    n = w.shape[0]
+    _need(w.shape[1] == k and x.stride(1) == 1 and w.stride(1) == 1, "x [M, K] and w [N, K], rows contiguous")
+    if y is None:
+        y = torch.empty(m, n, dtype=x.dtype, device=x.device)
+    _need(y.stride(1) == 1 and (residual is None or residual.stride(1) == 1), "rows of y and residual contiguous")
+    _check("tg_linear",
+           lib.tg_linear(_dtype_code(x), m, n, k, _ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(residual),
+                         residual.stride(0) if residual is not None else 0, _ptr(y), y.stride(0), _stream(x)))
+    return y
+
+
+def tg_swiglu(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, y: Optional[torch.Tensor] = None):
+    """y = SiLU(x Wg^T) * (x Wu^T); x [M, K], w_gate and w_up [F, K] with the same row stride."""
+    lib = load_library()
+    m, k = x.shape
+    f = w_gate.shape[0]
+    _need(tuple(w_up.shape) == tuple(w_gate.shape) and w_up.stride(0) == w_gate.stride(0), "w_gate, w_up alike")
+    _need(x.stride(1) == 1 and w_gate.stride(1) == 1 and w_up.stride(1) == 1, "rows contiguous")
+    if y is None:
+        y = torch.empty(m, f, dtype=x.dtype, device=x.device)
+    _check("tg_swiglu",
+           lib.tg_swiglu(_dtype_code(x), m, f, k, _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+                         _ptr(y), y.stride(0), _stream(x)))
+    return y

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtokengate.so")
 
 ARCH = "gfx950"
-SOURCES = ["tg_api.cpp", "gate.hip", "select.hip", "gather.hip", "rope.hip", "attn.hip", "decode.hip"]
+SOURCES = ["tg_api.cpp", "gate.hip", "select.hip", "gather.hip", "rope.hip", "attn.hip", "decode.hip", "dense.hip"]
 
 
 def _hipcc() -> str:

@@ -324,4 +324,47 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
                   "decode");
 }
 
+// ---------------------------------------------------------------------------
+static tg_status check_dense(const char* what, tg_dtype dtype, int64_t m, int64_t n, int64_t k, int n_mult,
+                             const void* x, int64_t ld_x, const void* w, int64_t ld_w, void* y, int64_t ld_y) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
+  if (dtype != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "%s: only TG_BF16 is implemented", what);
+  if (m < 0 || m > kMaxI32 || n <= 0 || k <= 0)
+    return fail(TG_ERR_INVALID_ARG, "%s: m=%lld, n=%lld, k=%lld out of range", what, (long long)m, (long long)n,
+                (long long)k);
+  if (n % n_mult != 0 || k % 32 != 0)
+    return fail(TG_ERR_UNSUPPORTED, "%s: n=%lld must be a multiple of %d and k=%lld of 32", what, (long long)n,
+                n_mult, (long long)k);
+  if (ld_x < k || ld_w < k || ld_y < n || ld_x % 8 != 0 || ld_w % 8 != 0)
+    return fail(TG_ERR_INVALID_ARG, "%s: leading dimensions too small or not multiples of 8", what);
+  if (!x || !w || !y) return fail(TG_ERR_INVALID_ARG, "%s: NULL pointer argument", what);
+  if (!aligned16(x) || !aligned16(w)) return fail(TG_ERR_INVALID_ARG, "%s: x and w must be 16-byte aligned", what);
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) != 0) return fail(TG_ERR_INVALID_ARG, "%s: y must be 2-byte aligned", what);
+  return TG_OK;
+}
+
+TG_API tg_status tg_linear(tg_dtype dtype, int64_t m, int32_t n, int32_t k, const void* x, int64_t ld_x,
+                           const void* w, int64_t ld_w, const void* residual, int64_t ld_r, void* y, int64_t ld_y,
+                           hipStream_t stream) {
+  tg_status st = check_dense("linear", dtype, m, n, k, 256, x, ld_x, w, ld_w, y, ld_y);
+  if (st != TG_OK) return st;
+  if (residual && (ld_r < n || (reinterpret_cast<uintptr_t>(residual) & 1u) != 0))
+    return fail(TG_ERR_INVALID_ARG, "linear: residual needs ld_r >= n and 2-byte alignment");
+  if (m == 0) return ok();
+  return from_hip(tg::launch_gemm_bf16(residual ? 1 : 0, m, n, k, x, ld_x, w, nullptr, ld_w, residual, ld_r, y,
+                                       ld_y, stream),
+                  "linear");
+}
+
+TG_API tg_status tg_swiglu(tg_dtype dtype, int64_t m, int32_t f, int32_t k, const void* x, int64_t ld_x,
+                           const void* w_gate, const void* w_up, int64_t ld_w, void* y, int64_t ld_y,
+                           hipStream_t stream) {
+  tg_status st = check_dense("swiglu", dtype, m, f, k, 128, x, ld_x, w_gate, ld_w, y, ld_y);
+  if (st != TG_OK) return st;
+  if (!w_up || !aligned16(w_up)) return fail(TG_ERR_INVALID_ARG, "swiglu: w_up must be 16-byte aligned, not NULL");
+  if (m == 0) return ok();
+  return from_hip(
+      tg::launch_gemm_bf16(2, m, f, k, x, ld_x, w_gate, w_up, ld_w, nullptr, 0, y, ld_y, stream), "swiglu");
+}
+
 }  // extern "C"

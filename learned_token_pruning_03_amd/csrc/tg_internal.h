@@ -115,4 +115,10 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
                          const float* g, const float* head_gain, void* o, float* lse, float* workspace,
                          hipStream_t stream);
 
+// Dense product C = A W^T on bf16 with an epilogue: 0 plain, 1 residual add,
+// 2 SwiGLU (w = gate weights, w2 = up weights, n = F).
+hipError_t launch_gemm_bf16(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* w,
+                            const void* w2, int64_t ldw, const void* r, int64_t ldr, void* c, int64_t ldc,
+                            hipStream_t stream);
+
 }  // namespace tg

@@ -110,6 +110,14 @@ def gate_weights(d: int, hidden: int, dtype: torch.dtype, seed: int):
     return w1, b1, w2, 0.0
 
 
+def linear_weight(n_out: int, n_in: int, dtype: torch.dtype, seed: int):
+    """A random-init projection weight [n_out, n_in] (nn.Linear layout),
+    N(0, 1/n_in) so that outputs of N(0, 1) inputs stay O(1)."""
+    g = _gen(seed * 7919 + 11)
+    w = torch.randn(n_out, n_in, generator=g, dtype=torch.float32) / math.sqrt(n_in)
+    return w.to(dtype).contiguous()
+
+
 def hidden_states(n: int, d: int, dtype: torch.dtype, seed: int,
                   planted_frac: float = 0.0, planted_scale: float = 8.0):
     """h [n, d] ~ N(0, 1); ``round(planted_frac * n)`` rows, chosen by the seed

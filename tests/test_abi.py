@@ -27,6 +27,7 @@ def test_header_declares_the_expected_entry_points():
     for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
+                 "tg_linear", "tg_swiglu",
                  "tg_status_string",
                  "tg_last_error", "tg_abi_version"):
         assert name in syms
@@ -128,6 +129,28 @@ def test_decode_validation_without_a_gpu(lib):
     assert call(ws_bytes=ws - 4) == tg.TG_ERR_INVALID_ARG
     assert b"workspace" in lib.tg_last_error()
     assert call(max_seqlen=-1) == tg.TG_ERR_INVALID_ARG
+
+
+def test_dense_validation_without_a_gpu(lib):
+    # tg_linear(dtype, m, n, k, x, ld_x, w, ld_w, residual, ld_r, y, ld_y, stream)
+    def lin(dtype=tg.TG_BF16, m=64, n=256, k=64, x=FAKE, ld_x=64, w=FAKE, ld_w=64, r=None, ld_r=0, ld_y=256):
+        return lib.tg_linear(dtype, m, n, k, x, ld_x, w, ld_w, r, ld_r, FAKE, ld_y, None)
+
+    assert lin(m=0) == tg.TG_OK
+    assert lin(dtype=tg.TG_FP32) == tg.TG_ERR_UNSUPPORTED
+    assert lin(n=320) == tg.TG_ERR_UNSUPPORTED
+    assert lin(k=48, ld_x=48, ld_w=48) == tg.TG_ERR_UNSUPPORTED
+    assert lin(ld_x=32) == tg.TG_ERR_INVALID_ARG
+    assert lin(ld_x=68) == tg.TG_ERR_INVALID_ARG  # rows not 16-byte aligned
+    assert lin(ld_y=128) == tg.TG_ERR_INVALID_ARG
+    assert lin(x=None) == tg.TG_ERR_INVALID_ARG
+    assert lin(x=FAKE + 8) == tg.TG_ERR_INVALID_ARG
+    assert lin(r=FAKE, ld_r=100) == tg.TG_ERR_INVALID_ARG
+    assert lin(m=-1) == tg.TG_ERR_INVALID_ARG
+    # tg_swiglu(dtype, m, f, k, x, ld_x, w_gate, w_up, ld_w, y, ld_y, stream)
+    assert lib.tg_swiglu(tg.TG_BF16, 0, 128, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 128, None) == tg.TG_OK
+    assert lib.tg_swiglu(tg.TG_BF16, 8, 192, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 192, None) == tg.TG_ERR_UNSUPPORTED
+    assert lib.tg_swiglu(tg.TG_BF16, 8, 128, 64, FAKE, 64, FAKE, None, 64, FAKE, 128, None) == tg.TG_ERR_INVALID_ARG
 
 
 def test_gather_and_rope_validation(lib):

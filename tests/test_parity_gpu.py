@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import learned_token_pruning_03_amd.workloads as W
-from oracle import ref_attn, ref_attn_varlen, ref_decode, ref_gate, ref_gather, ref_rope, ref_select, ref_select_varlen
+from oracle import ref_attn, ref_attn_varlen, ref_decode, ref_gate, ref_linear, ref_mlp, ref_swiglu, ref_gather, ref_rope, ref_select, ref_select_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -553,3 +553,89 @@ def test_decode_reuses_a_dirty_workspace(gpu_lib):
         torch.cuda.synchronize()
         o_ref, _ = ref_decode(q, k, v, g, cu)
         assert np.max(np.abs(o.cpu().double().numpy() - o_ref)) <= 2e-2
+
+
+# ----------------------------------------------------------------------------- dense (upper layers)
+def _dense_ok(got, want, slack=1e-3):
+    """One bf16 rounding of the fp32-accumulated result: |got - want| <= 2^-8 |want|
+    plus `slack` times the output's rms for values near zero."""
+    got = np.asarray(got, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(want ** 2))) + 1e-30
+    excess = np.abs(got - want) - (2.0 ** -8 * np.abs(want) + slack * rms)
+    _say("  max abs err", float(np.max(np.abs(got - want))), "rms", rms, "worst excess", float(np.max(excess)))
+    return bool(np.all(excess <= 0))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 32), (300, 256, 64), (129, 512, 2048), (4133, 4096, 256),
+                                   (1000, 2048, 6144)])
+def test_linear_parity(gpu_lib, m, n, k):
+    _say("linear", m, n, k)
+    x = W.hidden_states(m, k, torch.bfloat16, m + k)
+    w = W.linear_weight(n, k, torch.bfloat16, n + k)
+    y = gpu_lib.tg_linear(x.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    assert _dense_ok(y.cpu().double().numpy(), ref_linear(x, w))
+
+
+@pytest.mark.parametrize("m,n,k,inplace", [(300, 256, 64, False), (4133, 4096, 256, True), (777, 2048, 512, True)])
+def test_linear_residual_parity(gpu_lib, m, n, k, inplace):
+    _say("linear + residual", m, n, k, "in place" if inplace else "")
+    x = W.hidden_states(m, k, torch.bfloat16, 5 + m)
+    w = W.linear_weight(n, k, torch.bfloat16, 6 + n)
+    r = W.hidden_states(m, n, torch.bfloat16, 7 + k)
+    want = ref_linear(x, w, r)
+    rd = r.to(DEV)
+    y = gpu_lib.tg_linear(x.to(DEV), w.to(DEV), residual=rd, y=rd if inplace else None)
+    torch.cuda.synchronize()
+    assert _dense_ok(y.cpu().double().numpy(), want)
+
+
+@pytest.mark.parametrize("m,f,k", [(300, 128, 64), (129, 256, 2048), (4133, 6144, 256), (64, 768, 96)])
+def test_swiglu_parity(gpu_lib, m, f, k):
+    _say("swiglu", m, f, k)
+    x = W.hidden_states(m, k, torch.bfloat16, 9 + m)
+    wg = W.linear_weight(f, k, torch.bfloat16, 10 + f)
+    wu = W.linear_weight(f, k, torch.bfloat16, 11 + f)
+    y = gpu_lib.tg_swiglu(x.to(DEV), wg.to(DEV), wu.to(DEV))
+    torch.cuda.synchronize()
+    assert _dense_ok(y.cpu().double().numpy(), ref_swiglu(x, wg, wu))
+
+
+def test_linear_strided_operands(gpu_lib):
+    # Row strides of x, w and y larger than the logical widths (views into
+    # wider buffers), as when q, k and v are column slices of one projection.
+    m, n, k = 300, 256, 128
+    xb = W.hidden_states(m, k + 64, torch.bfloat16, 21)
+    wb = W.linear_weight(n, k + 32, torch.bfloat16, 22)
+    x, w = xb[:, 32:32 + k], wb[:, :k]
+    yb = torch.zeros(m, n + 256, dtype=torch.bfloat16, device=DEV)
+    gpu_lib.tg_linear(xb.to(DEV)[:, 32:32 + k], wb.to(DEV)[:, :k], y=yb[:, 256:])
+    torch.cuda.synchronize()
+    assert _dense_ok(yb[:, 256:].cpu().double().numpy(), ref_linear(x, w))
+    assert torch.all(yb[:, :256] == 0)  # nothing written outside y
+
+
+def test_mlp_block_qwen_shape_sampled_rows(gpu_lib):
+    # The MLP block of one upper layer at the bench shape: 4096 kept tokens,
+    # d = 2048, F = 6144: SwiGLU, then the down projection onto the residual
+    # stream in place.  The oracle checks 48 sampled rows (first, last, tile
+    # boundaries and random ones).
+    m, d, f = 4096, 2048, 6144
+    x = W.hidden_states(m, d, torch.bfloat16, 31)
+    wg = W.linear_weight(f, d, torch.bfloat16, 32)
+    wu = W.linear_weight(f, d, torch.bfloat16, 33)
+    wd = W.linear_weight(d, f, torch.bfloat16, 34)
+    res = W.hidden_states(m, d, torch.bfloat16, 35)
+    xd, resd = x.to(DEV), res.to(DEV)
+    a = gpu_lib.tg_swiglu(xd, wg.to(DEV), wu.to(DEV))
+    gpu_lib.tg_linear(a, wd.to(DEV), residual=resd, y=resd)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, m - 1],
+                                     np.random.default_rng(36).choice(m, 42, replace=False)]))
+    want = ref_mlp(x[rows], wg, wu, wd, res[rows])
+    # The hidden activation is stored in bf16 between the two products (as the
+    # layer stores it); its rounding (2^-9 relative per element) reaches the
+    # output as noise of ~1e-3 of the output's rms, hence the wider slack.
+    assert _dense_ok(resd.cpu()[rows].double().numpy(), want, slack=1e-2)
+    # The hidden activation itself, on the same rows.
+    assert _dense_ok(a.cpu()[rows].double().numpy(), ref_swiglu(x[rows], wg, wu))
