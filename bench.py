@@ -41,7 +41,7 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="qwen1p7b_32k", choices=["qwen1p7b_32k", "qwen1p7b_128k", "stack19"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-full-context", action="store_true",
-                   help="skip the comparison with one ungated layer over all N tokens")
+                   help="skip the comparison of one upper layer on the K kept tokens with one on all N tokens")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the decode attention figure over compact KV caches")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
@@ -180,32 +180,62 @@ def time_stages(path, reps):
     return {n: statistics.median(v) for n, v in samples.items()}, {n: sum(v) / len(v) for n, v in samples.items()}
 
 
-def full_context(tg, W, sh, dev, reps=8):
-    """One upper layer without pruning: RoPE + KV cache and ungated causal GQA
-    attention over all N prompt tokens (the same layer shape), medians of
-    event-timed repetitions.  The pruned path runs the same two stages on K."""
+FFN = 6144  # SwiGLU width of the Qwen3-1.7B-shaped upper layer (d = 2048)
+
+
+def upper_layer(tg, W, sh, dev, m, gated, reps=8):
+    """One upper layer of the Qwen3-1.7B shape on m token rows, every stage in
+    the library: fused QKV projection -> RoPE + KV cache -> attention (gated
+    on the kept tokens, ungated over the full prompt) -> O projection onto the
+    residual stream -> SwiGLU -> down projection onto the residual stream.
+    Medians of event-timed repetitions per stage.  RMSNorms are not included."""
+    import numpy as np
     import torch
-    q, k, v = W.qkv(sh.n, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 7)
-    q, k, v = q.to(dev), k.to(dev), v.to(dev)
-    kc, vc, o = torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
-    pos = torch.arange(sh.n, dtype=torch.int32, device=dev)
-    table = tg.tg_rope_table(sh.n, sh.dh, sh.rope_base, dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    rope_t, attn_t = [], []
+    d, hq, hkv, dh = sh.d, sh.hq, sh.hkv, sh.dh
+    x = W.hidden_states(m, d, sh.dtype, 21).to(dev)
+    w_qkv = W.linear_weight((hq + 2 * hkv) * dh, d, sh.dtype, 22).to(dev)
+    w_o = W.linear_weight(d, hq * dh, sh.dtype, 23).to(dev)
+    w_g = W.linear_weight(FFN, d, sh.dtype, 24).to(dev)
+    w_u = W.linear_weight(FFN, d, sh.dtype, 25).to(dev)
+    w_d = W.linear_weight(d, FFN, sh.dtype, 26).to(dev)
+    if gated:
+        pos = np.sort(np.random.default_rng(27).choice(sh.n, m, replace=False)).astype(np.int32)
+        g = W.random_scores(m, 28).to(dev)
+    else:
+        pos, g = np.arange(m, dtype=np.int32), None
+    pos = torch.from_numpy(pos).to(dev)
+    table = tg.tg_rope_table(sh.n, dh, sh.rope_base, dev)
+    q = torch.empty(m, hq, dh, dtype=sh.dtype, device=dev)
+    k, v = (torch.empty(m, hkv, dh, dtype=sh.dtype, device=dev) for _ in range(2))
+    kc, vc = torch.empty_like(k), torch.empty_like(v)
+    o = torch.empty_like(q)
+    a = torch.empty(m, FFN, dtype=sh.dtype, device=dev)
+    stages = [
+        ("qkv_proj", lambda: tg.tg_qkv_proj(x, w_qkv, hq, hkv, dh, q=q, k=k, v=v)),
+        ("rope_kv", lambda: tg.tg_rope_kv(q, k, v, pos, table, k_cache=kc, v_cache=vc)),
+        ("attn", lambda: tg.tg_gated_attn(q, kc, vc, g, pos, o=o)),
+        ("o_proj", lambda: tg.tg_linear(o.view(m, hq * dh), w_o, residual=x, y=x)),
+        ("swiglu", lambda: tg.tg_swiglu(x, w_g, w_u, y=a)),
+        ("down_proj", lambda: tg.tg_linear(a, w_d, residual=x, y=x)),
+    ]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    times = {n: [] for n, _ in stages}
     for r in range(reps + 1):
         ev[0].record()
-        tg.tg_rope_kv(q, k, v, pos, table, k_cache=kc, v_cache=vc)
-        ev[1].record()
-        tg.tg_gated_attn(q, kc, vc, None, pos, o=o)
-        ev[2].record()
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         if r:
-            rope_t.append(ev[0].elapsed_time(ev[1]) * 1e3)
-            attn_t.append(ev[1].elapsed_time(ev[2]) * 1e3)
-    flops = 4.0 * sh.dh * sh.hq * sh.n * (sh.n + 1) / 2.0
-    a = statistics.median(attn_t)
-    return {"n": sh.n, "rope_kv_us": round(statistics.median(rope_t), 2), "attn_us": round(a, 2),
-            "attn_TFLOP/s": round(flops / (a * 1e-6) / 1e12, 1)}
+            for i, (n, _) in enumerate(stages):
+                times[n].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+    med = {n: round(statistics.median(t), 2) for n, t in times.items()}
+    dense_flops = 2.0 * m * d * ((hq + 2 * hkv) * dh + hq * dh + 3 * FFN)
+    dense_us = med["qkv_proj"] + med["o_proj"] + med["swiglu"] + med["down_proj"]
+    attn_flops = 4.0 * dh * hq * m * (m + 1) / 2.0
+    return {"rows": m, "gated": gated, "stage_us": med, "total_us": round(sum(med.values()), 2),
+            "dense_us": round(dense_us, 2), "dense_TFLOP/s": round(dense_flops / (dense_us * 1e-6) / 1e12, 1),
+            "attn_TFLOP/s": round(attn_flops / (med["attn"] * 1e-6) / 1e12, 1)}
 
 
 def decode_step(tg, W, sh, dev, batch=32, reps=20):
@@ -454,16 +484,22 @@ def main(argv=None):
             e["TFLOP/s"] = round(fl_attn / (med[n] * 1e-6) / 1e12, 1)
         stages[n] = e
 
-    full = None
+    full = upper = None
     if not args.no_full_context:
-        print("[bench] timing one ungated layer over all N tokens ...", file=sys.stderr, flush=True)
-        full = full_context(tg, W, sh, dev)
+        print("[bench] timing one upper layer on the K kept tokens and on all N tokens ...", file=sys.stderr,
+              flush=True)
+        up_k = upper_layer(tg, W, sh, dev, sh.k, gated=True)
+        up_n = upper_layer(tg, W, sh, dev, sh.n, gated=False)
         layer_gated = med["rope_kv"] + med["attn"]
+        full = {"n": sh.n, "rope_kv_us": up_n["stage_us"]["rope_kv"], "attn_us": up_n["stage_us"]["attn"],
+                "attn_TFLOP/s": up_n["attn_TFLOP/s"]}
         full["layer_us"] = round(full["rope_kv_us"] + full["attn_us"], 2)
         full["layer_speedup_vs_pruned"] = round(full["layer_us"] / layer_gated, 2)
         # One selection layer's overhead (gate, select, gather) is paid once per
         # prompt; every upper layer then runs on K tokens instead of N.
         full["pruning_overhead_us"] = round(med["gate"] + med["select"] + med["gather"], 2)
+        upper = {"ffn": FFN, "pruned": up_k, "full": up_n,
+                 "layer_speedup_vs_pruned": round(up_n["total_us"] / up_k["total_us"], 2)}
 
     dec = None
     if not args.no_decode:
@@ -495,6 +531,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "stages": stages,
         "full_context": full,
+        "upper_layer": upper,
         "decode": dec,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "gate_pct_hbm_peak": round(100 * by["gate"] / (med["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),

@@ -339,6 +339,17 @@ TG_API tg_status tg_swiglu(tg_dtype dtype, int64_t m, int32_t f, int32_t k, cons
                            int64_t ld_x, const void* w_gate, const void* w_up, int64_t ld_w,
                            void* y, int64_t ld_y, hipStream_t stream);
 
+/* The fused QKV projection of an upper layer: one product with the stacked
+ * weight w_qkv = [Wq; Wk; Wv] ([(hq + 2 hkv) dh, ld_w], nn.Linear layout) whose
+ * output columns go straight to the three buffers tg_rope_kv and the
+ * attention read:  q [m, hq, dh], k_out [m, hkv, dh], v_out [m, hkv, dh]
+ * (contiguous, bf16).  hq*dh and hkv*dh must be multiples of 256; other
+ * arguments and errors as tg_linear (n = (hq + 2 hkv) dh). */
+TG_API tg_status tg_qkv_proj(tg_dtype dtype, int64_t m, int32_t hq, int32_t hkv, int32_t dh,
+                             int32_t k, const void* x, int64_t ld_x, const void* w_qkv,
+                             int64_t ld_w, void* q, void* k_out, void* v_out,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

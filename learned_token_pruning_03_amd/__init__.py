@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     tg_gather,
     tg_gather_varlen,
     tg_linear,
+    tg_qkv_proj,
     tg_rope_kv,
     tg_rope_table,
     tg_select_topk,

@@ -54,6 +54,8 @@ SIGNATURES = {
                    _c_vp], ctypes.c_int),
     "tg_swiglu": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
                   ctypes.c_int),
+    "tg_qkv_proj": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp,
+                     _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_decode_attn_workspace_size": ([_c_i32, _c_i64, _c_i32, _c_i32, _c_i32], _c_i64),
     "tg_decode_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
@@ -357,3 +359,20 @@ def tg_swiglu(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, y: Opti
            lib.tg_swiglu(_dtype_code(x), m, f, k, _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
                          _ptr(y), y.stride(0), _stream(x)))
     return y
+
+
+def tg_qkv_proj(x: torch.Tensor, w_qkv: torch.Tensor, hq: int, hkv: int, dh: int,
+                q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None):
+    """q [M, hq, dh], k and v [M, hkv, dh] from one product with w_qkv [(hq + 2 hkv) dh, K]."""
+    lib = load_library()
+    m, kin = x.shape
+    _need(tuple(w_qkv.shape) == ((hq + 2 * hkv) * dh, kin) and x.stride(1) == 1 and w_qkv.stride(1) == 1,
+          "x [M, K], w_qkv [(hq + 2 hkv) dh, K]")
+    q = torch.empty(m, hq, dh, dtype=x.dtype, device=x.device) if q is None else q
+    k = torch.empty(m, hkv, dh, dtype=x.dtype, device=x.device) if k is None else k
+    v = torch.empty(m, hkv, dh, dtype=x.dtype, device=x.device) if v is None else v
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v contiguous")
+    _check("tg_qkv_proj",
+           lib.tg_qkv_proj(_dtype_code(x), m, hq, hkv, dh, kin, _ptr(x), x.stride(0), _ptr(w_qkv), w_qkv.stride(0),
+                           _ptr(q), _ptr(k), _ptr(v), _stream(x)))
+    return q, k, v

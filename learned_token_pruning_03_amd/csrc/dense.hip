@@ -44,8 +44,11 @@ struct GemmArgs {
   const uint16_t* w;   // [N, Kin], or Wg [F, Kin] for swiglu
   const uint16_t* w2;  // Wu [F, Kin] for swiglu
   const uint16_t* r;   // residual [M, N]
-  uint16_t* c;
-  int64_t lda, ldw, ldr, ldc;
+  uint16_t* c;   // output columns [0, s1)
+  uint16_t* c1;  // output columns [s1, s2) (plain epilogue; s1 = s2 = n when unused)
+  uint16_t* c2;  // output columns [s2, n)
+  int64_t lda, ldw, ldr, ldc, ld1, ld2;
+  int s1, s2;
   int m, n, k;  // n = output columns (F for swiglu)
   int tiles_m, tiles_n;
 };
@@ -208,14 +211,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs p) {
   step(kt, ML{});
 
   // ---- epilogue.  acc[i][j][e] holds row wm*BM/2 + i*32 + 8*(e/4) + 4*half +
-  // e%4 of the tile and column (W row) wrow(j).
+  // e%4 of the tile and column (W row) wrow(j).  A 256-column tile lies in one
+  // of the (up to) three output ranges; pick its buffer once.
+  uint16_t* cbase = p.c;
+  int64_t ldo = p.ldc;
+  int c0 = 0;
+  if (EPI == kEpiPlain && n0 >= p.s2) {
+    cbase = p.c2;
+    ldo = p.ld2;
+    c0 = p.s2;
+  } else if (EPI == kEpiPlain && n0 >= p.s1) {
+    cbase = p.c1;
+    ldo = p.ld1;
+    c0 = p.s1;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
       if (row >= p.m) continue;
-      uint16_t* crow = p.c + (int64_t)row * p.ldc;
+      uint16_t* crow = cbase + (int64_t)row * ldo;
       if (EPI == kEpiSwiglu) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -232,7 +248,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs p) {
           const int col = n0 + wn * 128 + j * 32 + r32;
           float v = acc[i][j][e];
           if (EPI == kEpiResidual) v += bf16_bits_to_f32(rrow[col]);
-          reinterpret_cast<__bf16*>(crow)[col] = (__bf16)v;
+          reinterpret_cast<__bf16*>(crow)[col - c0] = (__bf16)v;
         }
       }
     }
@@ -261,7 +277,21 @@ hipError_t launch_epi(const GemmArgs& p, hipStream_t stream) {
 hipError_t launch_gemm_bf16(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* w,
                             const void* w2, int64_t ldw, const void* r, int64_t ldr, void* c, int64_t ldc,
                             hipStream_t stream) {
+  return launch_gemm_bf16_split(epi, m, n, k, a, lda, w, w2, ldw, r, ldr, c, ldc, nullptr, 0, n, nullptr, 0, n,
+                                stream);
+}
+
+hipError_t launch_gemm_bf16_split(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                                  const void* w, const void* w2, int64_t ldw, const void* r, int64_t ldr, void* c,
+                                  int64_t ldc, void* c1, int64_t ld1, int64_t s1, void* c2, int64_t ld2, int64_t s2,
+                                  hipStream_t stream) {
   GemmArgs p;
+  p.c1 = static_cast<uint16_t*>(c1);
+  p.c2 = static_cast<uint16_t*>(c2);
+  p.ld1 = ld1;
+  p.ld2 = ld2;
+  p.s1 = (int)s1;
+  p.s2 = (int)s2;
   p.a = static_cast<const uint16_t*>(a);
   p.w = static_cast<const uint16_t*>(w);
   p.w2 = static_cast<const uint16_t*>(w2);

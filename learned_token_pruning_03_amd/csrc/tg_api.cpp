@@ -367,4 +367,21 @@ TG_API tg_status tg_swiglu(tg_dtype dtype, int64_t m, int32_t f, int32_t k, cons
       tg::launch_gemm_bf16(2, m, f, k, x, ld_x, w_gate, w_up, ld_w, nullptr, 0, y, ld_y, stream), "swiglu");
 }
 
+TG_API tg_status tg_qkv_proj(tg_dtype dtype, int64_t m, int32_t hq, int32_t hkv, int32_t dh, int32_t k,
+                             const void* x, int64_t ld_x, const void* w_qkv, int64_t ld_w, void* q, void* k_out,
+                             void* v_out, hipStream_t stream) {
+  if (hq <= 0 || hkv <= 0 || dh <= 0 || ((int64_t)hq * dh) % 256 != 0 || ((int64_t)hkv * dh) % 256 != 0)
+    return fail(TG_ERR_UNSUPPORTED, "qkv_proj: hq*dh and hkv*dh must be positive multiples of 256");
+  const int64_t nq = (int64_t)hq * dh, nkv = (int64_t)hkv * dh, n = nq + 2 * nkv;
+  if (n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "qkv_proj: too many output columns");
+  tg_status st = check_dense("qkv_proj", dtype, m, n, k, 256, x, ld_x, w_qkv, ld_w, q, n);
+  if (st != TG_OK) return st;
+  if (!k_out || !v_out || (reinterpret_cast<uintptr_t>(k_out) & 1u) || (reinterpret_cast<uintptr_t>(v_out) & 1u))
+    return fail(TG_ERR_INVALID_ARG, "qkv_proj: k_out and v_out must be 2-byte aligned, not NULL");
+  if (m == 0) return ok();
+  return from_hip(tg::launch_gemm_bf16_split(0, m, n, k, x, ld_x, w_qkv, nullptr, ld_w, nullptr, 0, q, nq, k_out,
+                                             nkv, nq, v_out, nkv, nq + nkv, stream),
+                  "qkv_proj");
+}
+
 }  // extern "C"

@@ -120,5 +120,11 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
 hipError_t launch_gemm_bf16(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* w,
                             const void* w2, int64_t ldw, const void* r, int64_t ldr, void* c, int64_t ldc,
                             hipStream_t stream);
+// Same, plain epilogue only, with the output columns split over three buffers:
+// [0, s1) -> c, [s1, s2) -> c1, [s2, n) -> c2 (s1, s2 multiples of 256).
+hipError_t launch_gemm_bf16_split(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                                  const void* w, const void* w2, int64_t ldw, const void* r, int64_t ldr, void* c,
+                                  int64_t ldc, void* c1, int64_t ld1, int64_t s1, void* c2, int64_t ld2, int64_t s2,
+                                  hipStream_t stream);
 
 }  // namespace tg

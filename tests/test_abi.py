@@ -27,7 +27,7 @@ def test_header_declares_the_expected_entry_points():
     for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
-                 "tg_linear", "tg_swiglu",
+                 "tg_linear", "tg_swiglu", "tg_qkv_proj",
                  "tg_status_string",
                  "tg_last_error", "tg_abi_version"):
         assert name in syms
@@ -151,6 +151,12 @@ def test_dense_validation_without_a_gpu(lib):
     assert lib.tg_swiglu(tg.TG_BF16, 0, 128, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 128, None) == tg.TG_OK
     assert lib.tg_swiglu(tg.TG_BF16, 8, 192, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 192, None) == tg.TG_ERR_UNSUPPORTED
     assert lib.tg_swiglu(tg.TG_BF16, 8, 128, 64, FAKE, 64, FAKE, None, 64, FAKE, 128, None) == tg.TG_ERR_INVALID_ARG
+    # tg_qkv_proj(dtype, m, hq, hkv, dh, k, x, ld_x, w_qkv, ld_w, q, k_out, v_out, stream)
+    assert lib.tg_qkv_proj(tg.TG_BF16, 0, 16, 8, 128, 64, FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, None) == tg.TG_OK
+    assert lib.tg_qkv_proj(tg.TG_BF16, 8, 4, 2, 64, 64, FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE,
+                           None) == tg.TG_ERR_UNSUPPORTED  # hkv*dh = 128
+    assert lib.tg_qkv_proj(tg.TG_BF16, 8, 16, 8, 128, 64, FAKE, 64, FAKE, 64, FAKE, None, FAKE,
+                           None) == tg.TG_ERR_INVALID_ARG
 
 
 def test_gather_and_rope_validation(lib):

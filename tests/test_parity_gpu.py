@@ -639,3 +639,17 @@ def test_mlp_block_qwen_shape_sampled_rows(gpu_lib):
     assert _dense_ok(resd.cpu()[rows].double().numpy(), want, slack=1e-2)
     # The hidden activation itself, on the same rows.
     assert _dense_ok(a.cpu()[rows].double().numpy(), ref_swiglu(x[rows], wg, wu))
+
+
+@pytest.mark.parametrize("m,hq,hkv,dh,k", [(300, 16, 8, 128, 256), (4133, 16, 8, 128, 128), (77, 8, 4, 64, 64)])
+def test_qkv_proj_parity(gpu_lib, m, hq, hkv, dh, k):
+    _say("qkv_proj", m, hq, hkv, dh, k)
+    x = W.hidden_states(m, k, torch.bfloat16, 41 + m)
+    w = W.linear_weight((hq + 2 * hkv) * dh, k, torch.bfloat16, 42 + k)
+    q, kk, vv = gpu_lib.tg_qkv_proj(x.to(DEV), w.to(DEV), hq, hkv, dh)
+    torch.cuda.synchronize()
+    want = ref_linear(x, w)
+    nq, nkv = hq * dh, hkv * dh
+    assert _dense_ok(q.cpu().reshape(m, nq).double().numpy(), want[:, :nq])
+    assert _dense_ok(kk.cpu().reshape(m, nkv).double().numpy(), want[:, nq:nq + nkv])
+    assert _dense_ok(vv.cpu().reshape(m, nkv).double().numpy(), want[:, nq + nkv:])
