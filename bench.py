@@ -324,7 +324,43 @@ def cpu_baseline(W, name):
                    f"scaled to the full prompt"),
         "stage_s": {"gate": t_gate, "select": t_sel, "gather": t_gat, "rope_kv": t_rope, "attn": t_attn},
         "host_cpus": os.cpu_count(),
+        "next_rows": cpu_next_rows(W, sh),
     }
+
+
+def cpu_next_rows(W, sh, batch=32):
+    """The oracle on the two later rows the bench also times on the GPU, each on
+    a bounded sample scaled to the full call: decode attention (4 of the 32
+    sequences, caches of K keys) and one upper layer's dense work (QKV and O
+    projections, SwiGLU, down projection on 256 of the K kept rows)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    q, _, _ = W.qkv(4, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 12)
+    _, kc, vc = W.qkv(4 * sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 13)
+    g = W.random_scores(4 * sh.k, 14)
+    cu = np.arange(5) * sh.k
+    t0 = time.perf_counter()
+    O.ref_decode(q, kc, vc, g, cu)
+    t_dec = (time.perf_counter() - t0) * batch / 4
+    rows, d = 256, sh.d
+    x = W.hidden_states(rows, d, sh.dtype, 21)
+    w_qkv = W.linear_weight((sh.hq + 2 * sh.hkv) * sh.dh, d, sh.dtype, 22)
+    w_o = W.linear_weight(d, sh.hq * sh.dh, sh.dtype, 23)
+    w_g = W.linear_weight(FFN, d, sh.dtype, 24)
+    w_u = W.linear_weight(FFN, d, sh.dtype, 25)
+    w_d = W.linear_weight(d, FFN, sh.dtype, 26)
+    o = torch.zeros(rows, sh.hq * sh.dh, dtype=sh.dtype)
+    t0 = time.perf_counter()
+    O.ref_linear(x, w_qkv)
+    O.ref_linear(o, w_o, x)
+    O.ref_mlp(x, w_g, w_u, w_d, x)
+    t_dense = (time.perf_counter() - t0) * sh.k / rows
+    return {"decode_s": t_dec, "decode_tokens/s": batch / t_dec,
+            "upper_dense_s": t_dense, "upper_dense_rows": sh.k,
+            "sample": f"decode: 4 of {batch} sequences with {sh.k}-key caches, scaled by {batch // 4}; "
+                      f"dense: {rows} of {sh.k} kept rows, scaled by {sh.k // rows}"}
 
 
 def load_traffic():
