@@ -350,6 +350,19 @@ TG_API tg_status tg_qkv_proj(tg_dtype dtype, int64_t m, int32_t hq, int32_t hkv,
                              int64_t ld_w, void* q, void* k_out, void* v_out,
                              hipStream_t stream);
 
+/* Check of the position precondition of the attention entry points (the
+ * pages' causal mask is on original positions; with strictly increasing
+ * positions it equals the mask on kept indices, which the bf16 kernels use).
+ * Writes to *first_bad (device int32) the smallest row i that breaks the
+ * order -- pos[i] < 0, or pos[i] <= pos[i-1] with row i-1 in the same
+ * sequence -- or `total` when every row is in order.  cu_seqlens [batch+1]
+ * (device) splits the rows into sequences as in tg_gated_attn_varlen, or NULL
+ * for one sequence.  Two small kernels on `stream`; no synchronisation, no
+ * allocation.  Errors: TG_ERR_INVALID_ARG for NULL pointers or sizes out of
+ * range. */
+TG_API tg_status tg_check_positions(const int32_t* pos, int64_t total, const int32_t* cu_seqlens,
+                                    int32_t batch, int32_t* first_bad, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     TokenGateError,
     load_library,
     status_string,
+    tg_check_positions,
     tg_decode_attn,
     tg_decode_attn_workspace_size,
     tg_gate_score,

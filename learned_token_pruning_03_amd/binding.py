@@ -56,6 +56,7 @@ SIGNATURES = {
                   ctypes.c_int),
     "tg_qkv_proj": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp,
                      _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_check_positions": ([_c_vp, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "tg_decode_attn_workspace_size": ([_c_i32, _c_i64, _c_i32, _c_i32, _c_i32], _c_i64),
     "tg_decode_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
@@ -376,3 +377,17 @@ def tg_qkv_proj(x: torch.Tensor, w_qkv: torch.Tensor, hq: int, hkv: int, dh: int
            lib.tg_qkv_proj(_dtype_code(x), m, hq, hkv, dh, kin, _ptr(x), x.stride(0), _ptr(w_qkv), w_qkv.stride(0),
                            _ptr(q), _ptr(k), _ptr(v), _stream(x)))
     return q, k, v
+
+
+def tg_check_positions(pos: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                       first_bad: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device int32 [1]: the smallest row whose position breaks the strictly
+    increasing order within its sequence (or is negative), else len(pos)."""
+    lib = load_library()
+    _need(pos.dtype == torch.int32, "pos is int32")
+    if first_bad is None:
+        first_bad = torch.empty(1, dtype=torch.int32, device=pos.device)
+    batch = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check("tg_check_positions",
+           lib.tg_check_positions(_ptr(pos), pos.numel(), _ptr(cu_seqlens), batch, _ptr(first_bad), _stream(pos)))
+    return first_bad

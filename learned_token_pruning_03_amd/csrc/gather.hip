@@ -73,4 +73,47 @@ hipError_t launch_gather(int elem_bytes, int64_t n, int64_t n_kept, int d, const
   return hipGetLastError();
 }
 
+// ---- check of the attention entry points' position precondition ---------
+// Within each sequence the positions must be non-negative and strictly
+// increasing (the order select + gather produce).  The first kernel sets the
+// answer to `total` (no offending row); the second lowers it to the smallest
+// offending row with a vector atomic.
+namespace {
+
+__global__ __launch_bounds__(64) void check_pos_init_kernel(int32_t* bad, int32_t total) {
+  if (threadIdx.x == 0) *bad = total;
+}
+
+__global__ __launch_bounds__(256) void check_pos_kernel(const int32_t* __restrict__ pos, int32_t total,
+                                                        const int32_t* __restrict__ cu, int32_t batch,
+                                                        int32_t* bad) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  bool first = i == 0;
+  if (cu && !first) {  // largest b with cu[b] <= i; row i starts a sequence iff cu[b] == i
+    int lo = 0, hi = batch;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= i)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    first = cu[lo] == i;
+  }
+  const int32_t p = pos[i];
+  if (p < 0 || (!first && p <= pos[i - 1])) atomicMin(bad, (int32_t)i);
+}
+
+}  // namespace
+
+hipError_t launch_check_positions(const int32_t* pos, int64_t total, const int32_t* cu_seqlens, int batch,
+                                   int32_t* first_bad, hipStream_t stream) {
+  hipLaunchKernelGGL(check_pos_init_kernel, dim3(1), dim3(64), 0, stream, first_bad, (int32_t)total);
+  if (total > 0)
+    hipLaunchKernelGGL(check_pos_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, pos,
+                       (int32_t)total, cu_seqlens, batch, first_bad);
+  return hipGetLastError();
+}
+
 }  // namespace tg

@@ -384,4 +384,14 @@ TG_API tg_status tg_qkv_proj(tg_dtype dtype, int64_t m, int32_t hq, int32_t hkv,
                   "qkv_proj");
 }
 
+TG_API tg_status tg_check_positions(const int32_t* pos, int64_t total, const int32_t* cu_seqlens, int32_t batch,
+                                    int32_t* first_bad, hipStream_t stream) {
+  if (total < 0 || total > kMaxI32) return fail(TG_ERR_INVALID_ARG, "check_positions: total out of range");
+  if (!first_bad) return fail(TG_ERR_INVALID_ARG, "check_positions: NULL first_bad");
+  if (total > 0 && !pos) return fail(TG_ERR_INVALID_ARG, "check_positions: NULL pos");
+  if (cu_seqlens && batch < 0) return fail(TG_ERR_INVALID_ARG, "check_positions: negative batch");
+  return from_hip(tg::launch_check_positions(pos, total, cu_seqlens, cu_seqlens ? batch : 0, first_bad, stream),
+                  "check_positions");
+}
+
 }  // extern "C"

@@ -115,6 +115,11 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
                          const float* g, const float* head_gain, void* o, float* lse, float* workspace,
                          hipStream_t stream);
 
+// Writes the smallest row whose position breaks the strictly-increasing,
+// non-negative order within its sequence, or `total`.
+hipError_t launch_check_positions(const int32_t* pos, int64_t total, const int32_t* cu_seqlens, int batch,
+                                  int32_t* first_bad, hipStream_t stream);
+
 // Dense product C = A W^T on bf16 with an epilogue: 0 plain, 1 residual add,
 // 2 SwiGLU (w = gate weights, w2 = up weights, n = F).
 hipError_t launch_gemm_bf16(int epi, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* w,

@@ -27,7 +27,7 @@ def test_header_declares_the_expected_entry_points():
     for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
-                 "tg_linear", "tg_swiglu", "tg_qkv_proj",
+                 "tg_linear", "tg_swiglu", "tg_qkv_proj", "tg_check_positions",
                  "tg_status_string",
                  "tg_last_error", "tg_abi_version"):
         assert name in syms
@@ -157,6 +157,14 @@ def test_dense_validation_without_a_gpu(lib):
                            None) == tg.TG_ERR_UNSUPPORTED  # hkv*dh = 128
     assert lib.tg_qkv_proj(tg.TG_BF16, 8, 16, 8, 128, 64, FAKE, 64, FAKE, 64, FAKE, None, FAKE,
                            None) == tg.TG_ERR_INVALID_ARG
+
+
+def test_check_positions_validation_without_a_gpu(lib):
+    # tg_check_positions(pos, total, cu_seqlens, batch, first_bad, stream)
+    assert lib.tg_check_positions(FAKE, 10, None, 0, None, None) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_check_positions(None, 10, None, 0, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_check_positions(FAKE, -1, None, 0, FAKE, None) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_check_positions(FAKE, 10, FAKE, -2, FAKE, None) == tg.TG_ERR_INVALID_ARG
 
 
 def test_gather_and_rope_validation(lib):

@@ -653,3 +653,26 @@ def test_qkv_proj_parity(gpu_lib, m, hq, hkv, dh, k):
     assert _dense_ok(q.cpu().reshape(m, nq).double().numpy(), want[:, :nq])
     assert _dense_ok(kk.cpu().reshape(m, nkv).double().numpy(), want[:, nq:nq + nkv])
     assert _dense_ok(vv.cpu().reshape(m, nkv).double().numpy(), want[:, nq + nkv:])
+
+
+# ----------------------------------------------------------------------------- position check
+def test_check_positions(gpu_lib):
+    def run(pos, cu=None):
+        p = torch.tensor(pos, dtype=torch.int32, device=DEV)
+        c = None if cu is None else torch.tensor(cu, dtype=torch.int32, device=DEV)
+        return int(gpu_lib.tg_check_positions(p, c).item())
+
+    sparse = np.sort(np.random.default_rng(3).choice(40000, 5000, replace=False)).tolist()
+    assert run(sparse) == 5000  # select + gather order: valid
+    bad = list(sparse)
+    bad[3001] = bad[3000]  # repeated position
+    bad[4000] = -1
+    assert run(bad) == 3001
+    assert run([0, 5, 5]) == 2
+    assert run([3, 2, 1]) == 1
+    assert run([-4]) == 0
+    assert run([]) == 0
+    # Packed sequences: each restarts its positions; the order is checked within each.
+    assert run([0, 4, 9, 1, 2, 0, 7], cu=[0, 3, 5, 5, 7]) == 7
+    assert run([0, 4, 9, 1, 1, 0, 7], cu=[0, 3, 5, 5, 7]) == 4
+    assert run([0, 4, 9, 1, 2, 0, 0], cu=[0, 3, 5, 5, 7]) == 6
