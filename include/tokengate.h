@@ -5,7 +5,8 @@
  * Sources, cited by page title and section only:
  *   [paper]  "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
  *            with Learned Token Pruning" (paper page on thelatestinai.com),
- *            Abstract and Figure 1 (a)-(c).
+ *            Abstract, Figure 1 (a)-(c) and the training-setup table (base
+ *            model and LoRA configuration).
  *   [aitu]   The aitualizate.com news article on TokenGate, sections
  *            "2. Una red MLP aprende qué tokens conservar", "3. Las capas
  *            superiores procesan únicamente los tokens seleccionados",
@@ -35,6 +36,12 @@
  *    IEEE bfloat16 stored in 2 bytes; every fp32 -> bf16 conversion rounds to
  *    nearest even.  Tensor pointers must be 16-byte aligned.
  *  - Gate values g are fp32.  Indices and positions are int32.
+ *  - A packed ragged batch (cu_seqlens) holds at most 65535 prompts per call
+ *    (one launch-grid row per prompt); larger batches give TG_ERR_UNSUPPORTED.
+ *  - Later rows beside the prefill path: decode attention over the compact
+ *    cache (tg_decode_attn, the only call that takes a caller workspace), the
+ *    upper layers' dense products (tg_qkv_proj, tg_linear, tg_swiglu) and a
+ *    device-side check of the position order (tg_check_positions).
  */
 #ifndef TOKENGATE_H_
 #define TOKENGATE_H_
@@ -311,7 +318,8 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
  * taken as merged into W before the path (W + (alpha/r) B A).
  *
  * tg_linear:  y = x W^T            (residual NULL)
- *             y = x W^T + residual  (residual may equal y: in-place add)
+ *             y = x W^T + residual  (residual may equal y, with ld_r == ld_y:
+ *                                    in-place add)
  * tg_swiglu:  y = SiLU(x Wg^T) * (x Wu^T),  SiLU(z) = z / (1 + e^-z)
  * The MLP block is tg_swiglu followed by tg_linear with W_down and the
  * residual stream.

@@ -40,6 +40,7 @@ int elem_size(tg_dtype dt) { return dt == TG_BF16 ? 2 : 4; }
 bool valid_dtype(tg_dtype dt) { return dt == TG_BF16 || dt == TG_FP32; }
 
 constexpr int64_t kMaxI32 = 2147483647LL;
+constexpr int32_t kMaxGridYZ = 65535;  // launch grid limit in y and z (one prompt per index)
 
 }  // namespace
 
@@ -156,6 +157,7 @@ TG_API tg_status tg_gather_varlen(tg_dtype dtype, const int32_t* cu_seqlens, con
   if (batch < 0 || max_kept < 0 || max_kept > kMaxI32)
     return fail(TG_ERR_INVALID_ARG, "gather_varlen: batch or max_kept out of range");
   if (batch == 0 || max_kept == 0) return ok();
+  if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "gather_varlen: batch above %d", kMaxGridYZ);
   tg_status st = check_gather_common(dtype, d, h, ld_h, g, h_out, g_out);
   if (st != TG_OK) return st;
   if (!idx_local || !cu_seqlens || !cu_kept) return fail(TG_ERR_INVALID_ARG, "gather_varlen: NULL pointer argument");
@@ -248,6 +250,7 @@ TG_API tg_status tg_gated_attn_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
   if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32 || total < 0 || total > kMaxI32)
     return fail(TG_ERR_INVALID_ARG, "attn_varlen: batch, max_seqlen or total out of range");
   if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
+  if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "attn_varlen: batch above %d", kMaxGridYZ);
   tg_status st = check_attn(dtype, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o);
   if (st != TG_OK) return st;
   if (!cu_seqlens) return fail(TG_ERR_INVALID_ARG, "attn_varlen: NULL cu_seqlens");
@@ -266,6 +269,7 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
     if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32)
       return fail(TG_ERR_INVALID_ARG, "attn_ex: batch or max_seqlen out of range");
     if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
+    if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "attn_ex: batch above %d", kMaxGridYZ);
   } else {
     batch = 1;
     max_seqlen = total;
@@ -310,6 +314,7 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
   if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "decode: dh=%d must be 64 or 128", dh);
   if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "decode: scale must be > 0");
   if (batch == 0) return ok();
+  if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "decode: batch above %d", kMaxGridYZ);
   if (!cu_seqlens || !q || !k_cache || !v_cache || !o || !workspace)
     return fail(TG_ERR_INVALID_ARG, "decode: NULL pointer argument");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
@@ -337,6 +342,8 @@ static tg_status check_dense(const char* what, tg_dtype dtype, int64_t m, int64_
                 n_mult, (long long)k);
   if (ld_x < k || ld_w < k || ld_y < n || ld_x % 8 != 0 || ld_w % 8 != 0)
     return fail(TG_ERR_INVALID_ARG, "%s: leading dimensions too small or not multiples of 8", what);
+  if (((m + 127) / 128) * (n / 128) > kMaxI32)
+    return fail(TG_ERR_UNSUPPORTED, "%s: product too large for one launch", what);
   if (!x || !w || !y) return fail(TG_ERR_INVALID_ARG, "%s: NULL pointer argument", what);
   if (!aligned16(x) || !aligned16(w)) return fail(TG_ERR_INVALID_ARG, "%s: x and w must be 16-byte aligned", what);
   if ((reinterpret_cast<uintptr_t>(y) & 1u) != 0) return fail(TG_ERR_INVALID_ARG, "%s: y must be 2-byte aligned", what);
@@ -350,6 +357,8 @@ TG_API tg_status tg_linear(tg_dtype dtype, int64_t m, int32_t n, int32_t k, cons
   if (st != TG_OK) return st;
   if (residual && (ld_r < n || (reinterpret_cast<uintptr_t>(residual) & 1u) != 0))
     return fail(TG_ERR_INVALID_ARG, "linear: residual needs ld_r >= n and 2-byte alignment");
+  if (residual == y && ld_r != ld_y)
+    return fail(TG_ERR_INVALID_ARG, "linear: an in-place residual (residual == y) needs ld_r == ld_y");
   if (m == 0) return ok();
   return from_hip(tg::launch_gemm_bf16(residual ? 1 : 0, m, n, k, x, ld_x, w, nullptr, ld_w, residual, ld_r, y,
                                        ld_y, stream),

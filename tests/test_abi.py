@@ -129,6 +129,8 @@ def test_decode_validation_without_a_gpu(lib):
     assert call(ws_bytes=ws - 4) == tg.TG_ERR_INVALID_ARG
     assert b"workspace" in lib.tg_last_error()
     assert call(max_seqlen=-1) == tg.TG_ERR_INVALID_ARG
+    big = lib.tg_decode_attn_workspace_size(70000, 5000, 16, 8, 128)
+    assert call(batch=70000, ws_bytes=big) == tg.TG_ERR_UNSUPPORTED  # one grid row per sequence
 
 
 def test_dense_validation_without_a_gpu(lib):
@@ -147,6 +149,8 @@ def test_dense_validation_without_a_gpu(lib):
     assert lin(x=FAKE + 8) == tg.TG_ERR_INVALID_ARG
     assert lin(r=FAKE, ld_r=100) == tg.TG_ERR_INVALID_ARG
     assert lin(m=-1) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_linear(tg.TG_BF16, 64, 256, 64, FAKE, 64, FAKE, 64, FAKE + 4096, 512, FAKE + 4096, 256,
+                         None) == tg.TG_ERR_INVALID_ARG  # in-place residual with another stride
     # tg_swiglu(dtype, m, f, k, x, ld_x, w_gate, w_up, ld_w, y, ld_y, stream)
     assert lib.tg_swiglu(tg.TG_BF16, 0, 128, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 128, None) == tg.TG_OK
     assert lib.tg_swiglu(tg.TG_BF16, 8, 192, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 192, None) == tg.TG_ERR_UNSUPPORTED
