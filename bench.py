@@ -363,15 +363,16 @@ def cpu_next_rows(W, sh, batch=32):
                       f"dense: {rows} of {sh.k} kept rows, scaled by {sh.k // rows}"}
 
 
-def load_traffic():
+def load_traffic(workload):
     """HBM bytes per attention launch from the committed rocprofv3 PMC summary,
-    valid only while the attention kernel source is the one it was taken on."""
+    valid only for the workload it was taken on and while the attention kernel
+    source is the one it was taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != _file_sha(ATTN_KERNEL_SOURCE):
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256_16") != _file_sha(ATTN_KERNEL_SOURCE):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -497,7 +498,7 @@ def main(argv=None):
     fl_gate = gate_flops(sh)
     by = stage_bytes(sh)
     attn_tflops = fl_attn / (attn_avg_us * 1e-6) / 1e12
-    traffic = load_traffic()
+    traffic = load_traffic(args.workload)
     roofline = {
         "kernel": "attn_bf16_pp_kernel<128>",
         "bound": "mfma",

@@ -56,3 +56,12 @@ def test_traffic_summary_scales_each_counter_by_the_copy_kernel(tmp_path):
     assert rec["write_bytes_per_launch"] == 300 * 1024
     assert rec["hbm_bytes_per_launch"] == 2 * 1000 * 1024 + 300 * 1024
     assert rec["dispatches"] == {"fetch": 2, "write": 1}
+
+
+def test_stored_traffic_applies_only_to_its_workload_and_kernel_source():
+    # The committed PMC summary was taken on the 32k workload; other
+    # workloads get no traffic figure.
+    assert bench.load_traffic("qwen1p7b_128k") is None
+    assert bench.load_traffic("stack19") is None
+    t = bench.load_traffic("qwen1p7b_32k")
+    assert t is None or t > 0
