@@ -151,6 +151,40 @@ def stage_bytes(sh):
     }
 
 
+def graph_steps(torch, path, steps, warmup):
+    """The same step captured into one HIP graph per copy of h and replayed:
+    the launch sequence without the host's per-call overhead.  The captured
+    calls are the library's kernels only (no memset nodes)."""
+    copies = len(path.h)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(copies):  # warm-up on the capture stream
+            path.step_no = c
+            path.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        path.step_no = c
+        with torch.cuda.graph(g):
+            path.step()
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return {"ms_per_step": round(ms, 4), "tokens/s": round(path.sh.n / (ms * 1e-3), 1), "steps": steps}
+
+
 def time_stages(path, reps):
     import torch
     sh = path.sh
@@ -491,6 +525,9 @@ def main(argv=None):
     tokens_per_s = sh.n * args.steps / (ms_total / 1e3)
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
+    graph = graph_steps(torch, path, args.steps, args.warmup)
+    print(f"[bench] HIP graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
     med, mean = time_stages(path, args.stage_reps)
     print(f"[bench] stage medians (us): {json.dumps({k: round(v, 2) for k, v in med.items()})}",
           file=sys.stderr, flush=True)
@@ -567,6 +604,7 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "hip_graph": graph,
         "full_context": full,
         "upper_layer": upper,
         "decode": dec,

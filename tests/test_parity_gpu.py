@@ -676,3 +676,66 @@ def test_check_positions(gpu_lib):
     assert run([0, 4, 9, 1, 2, 0, 7], cu=[0, 3, 5, 5, 7]) == 7
     assert run([0, 4, 9, 1, 1, 0, 7], cu=[0, 3, 5, 5, 7]) == 4
     assert run([0, 4, 9, 1, 2, 0, 0], cu=[0, 3, 5, 5, 7]) == 6
+
+
+# ----------------------------------------------------------------------------- HIP graph replay
+def test_path_replayed_from_a_hip_graph(gpu_lib):
+    # The whole path (gate -> select -> gather -> RoPE + KV -> attention, plus
+    # decode over the cache it built) captured once into a HIP graph and
+    # replayed three times, with eager work and synchronisation between the
+    # replays.  Every replay must reproduce the eager outputs bit for bit.
+    tg = gpu_lib
+    n, q_len, d, hidden, k, hq, hkv, dh = 4096, 64, 2048, 256, 1024, 16, 8, 128
+    h = W.hidden_states(n, d, torch.bfloat16, 51, planted_frac=0.05).to(DEV)
+    w1, b1, w2, b2 = W.gate_weights(d, hidden, torch.bfloat16, 51)
+    w1, b1, w2 = w1.to(DEV), b1.to(DEV), w2.to(DEV)
+    q0, kk, vv = (t.to(DEV) for t in W.qkv(k, hq, hkv, dh, 1.0 / dh, torch.bfloat16, 52))
+    qn = W.qkv(1, hq, hkv, dh, 1.0 / dh, torch.bfloat16, 53)[0].to(DEV)
+    table = tg.tg_rope_table(n, dh, 1e6, DEV)
+    cu = torch.tensor([0, k], dtype=torch.int32, device=DEV)
+    ws = torch.empty(tg.tg_decode_attn_workspace_size(1, k, hq, hkv, dh), dtype=torch.uint8, device=DEV)
+
+    def buffers():
+        return {"g": torch.empty(n, device=DEV), "idx": torch.empty(k, dtype=torch.int32, device=DEV),
+                "hk": torch.empty(k, d, dtype=torch.bfloat16, device=DEV), "gk": torch.empty(k, device=DEV),
+                "pos": torch.empty(k, dtype=torch.int32, device=DEV), "q": torch.empty_like(q0),
+                "kc": torch.empty_like(kk), "vc": torch.empty_like(vv), "o": torch.empty_like(q0),
+                "lse": torch.empty(hq, k, device=DEV), "od": torch.empty_like(qn)}
+
+    def path(b):
+        b["q"].copy_(q0)  # RoPE rotates q in place: start every run from the same q
+        tg.tg_gate_score(h, w1, b1, w2, b2, g=b["g"])
+        tg.tg_select_topk(b["g"], k, q_len, idx=b["idx"])
+        tg.tg_gather(h, b["g"], b["idx"], h_out=b["hk"], g_out=b["gk"], pos_out=b["pos"])
+        tg.tg_rope_kv(b["q"], kk, vv, b["pos"], table, k_cache=b["kc"], v_cache=b["vc"])
+        tg.tg_gated_attn(b["q"], b["kc"], b["vc"], b["gk"], b["pos"], o=b["o"], lse=b["lse"])
+        tg.tg_decode_attn(qn, b["kc"], b["vc"], b["gk"], cu, k, o=b["od"], workspace=ws)
+
+    eager = buffers()
+    path(eager)
+    torch.cuda.synchronize()
+    want = {name: t.clone() for name, t in eager.items()}
+
+    graphed = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path(graphed)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path(graphed)
+    for rep in range(3):
+        for t in graphed.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say("graph replay", rep)
+        for name, t in graphed.items():
+            a, b = t.view(torch.uint8) if t.dtype != torch.bfloat16 else t.view(torch.int16), want[name]
+            b = b.view(torch.uint8) if b.dtype != torch.bfloat16 else b.view(torch.int16)
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
+        path(eager)  # eager work between replays
+        torch.cuda.synchronize()
