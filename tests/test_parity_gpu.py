@@ -739,3 +739,50 @@ def test_path_replayed_from_a_hip_graph(gpu_lib):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
         path(eager)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_end_to_end_ragged_batch_of_eight_prompts(gpu_lib):
+    """The packed-batch path at its configuration: 8 prompts of 4096-32768
+    tokens with 32-128-token question tails, K = 256 kept per prompt, each
+    stage checked against the oracle on the previous GPU stage's bytes."""
+    tg = gpu_lib
+    sh = W.SHAPES["ragged8"]
+    seed = W.SEEDS["ragged8"]
+    ns, qs = W.ragged_lengths(8, seed)
+    _say("end-to-end ragged8", ns, qs)
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    total = int(cu[-1])
+    h = W.hidden_states(total, sh.d, sh.dtype, seed)
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+    hd = h.to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    g = tg.tg_gate_score(hd, w1.to(DEV), b1.to(DEV), w2.to(DEV), b2)
+    kept_total = sum(min(sh.k, n) for n in ns)
+    idx, cu_kept = tg.tg_select_topk_varlen(g, cud, torch.tensor(qs, dtype=torch.int32, device=DEV), max(ns), sh.k,
+                                            kept_total)
+    hk, gk, pos = tg.tg_gather_varlen(hd, g, idx, cud, cu_kept, sh.k)
+    q, k, v = W.qkv(kept_total, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed)
+    table = tg.tg_rope_table(max(ns), sh.dh, sh.rope_base, DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    _, kc, vc = tg.tg_rope_kv(qd, kd, vd, pos, table)
+    o, lse = tg.tg_gated_attn_varlen(qd, kc, vc, gk, pos, cu_kept, sh.k, want_lse=True)
+    torch.cuda.synchronize()
+
+    # Gate on 2048 sampled rows (the oracle on all ~150k rows would take minutes).
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, np.random.default_rng(seed).choice(total, 2000,
+                                                                                          replace=False)]))
+    g_ref, _ = ref_gate(h[rows], w1, b1, w2, b2)
+    g_cpu = g.cpu().numpy()
+    assert _rel_err(g_cpu[rows], g_ref) <= 1e-2
+    idx_ref, cu_kept_ref = ref_select_varlen(g_cpu, cu, qs, sh.k)
+    np.testing.assert_array_equal(cu_kept.cpu().numpy(), cu_kept_ref)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    grow = np.concatenate([cu[b] + idx_ref[cu_kept_ref[b]:cu_kept_ref[b + 1]] for b in range(8)])
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16).numpy(), h.view(torch.int16).numpy()[grow])
+    np.testing.assert_array_equal(gk.cpu().numpy(), g_cpu[grow])
+    np.testing.assert_array_equal(pos.cpu().numpy(), idx_ref)
+    wq = ref_rope(q, idx_ref, sh.rope_base)
+    assert np.all(np.abs(qd.cpu().double().numpy() - wq) <= 2.0 ** -8 * np.abs(wq) + 1e-6)
+    wo, wl = ref_attn_varlen(qd.cpu(), kc.cpu(), vc.cpu(), g_cpu[grow], idx_ref, cu_kept_ref)
+    assert np.max(np.abs(o.cpu().double().numpy() - wo)) <= 2e-2
+    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= 1e-3
