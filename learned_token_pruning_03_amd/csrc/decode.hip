@@ -109,12 +109,15 @@ struct DecArgs {
 // GROUP = query heads per KV head (compile-time so that per-head state stays
 // in registers).  U = steps (of KPB keys) per loop iteration; the loads of
 // the next iteration are in flight while the current one is computed.
-template <typename T, int DH, int GROUP, int U>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
+// NW waves per workgroup.  FINAL: the workgroup holds the sequence's whole
+// cache (one block per sequence and KV head) and writes o and lse itself.
+template <typename T, int DH, int GROUP, int U, int NW, bool FINAL>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecArgs a) {
   constexpr int LPK = DH / 8;          // lanes per key row
   constexpr int KPW = kWave / LPK;     // key rows per wave per step
-  constexpr int KPB = KPW * kDecWaves; // key rows per workgroup per step
-  __shared__ float red[kDecWaves][GROUP][DH + 2];
+  constexpr int KPB = KPW * NW;        // key rows per workgroup per step
+  constexpr int NT = NW * 64;
+  __shared__ float red[NW][GROUP][DH + 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,7 +128,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
   const int64_t s0 = a.cu[b];
   const int L = a.cu[b + 1] - (int)s0;
   const int k0 = split * a.split;
-  if (k0 >= L) return;
+  if (k0 >= L) {
+    if (FINAL) {  // empty cache: o = 0, lse = -inf
+      for (int t = tid; t < GROUP * DH; t += NT) {
+        const int64_t oi = ((int64_t)b * a.hq + kvh * GROUP + t / DH) * DH + t % DH;
+        if constexpr (sizeof(T) == 2)
+          reinterpret_cast<__bf16*>(a.o)[oi] = (__bf16)0.0f;
+        else
+          reinterpret_cast<float*>(a.o)[oi] = 0.0f;
+      }
+      if (a.lse && tid < GROUP) a.lse[(int64_t)b * a.hq + kvh * GROUP + tid] = -INFINITY;
+    }
+    return;
+  }
   const int k1 = min(L, k0 + a.split);
   const float c = a.scale_log2;
 
@@ -232,26 +247,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
   __syncthreads();
   // Merge the waves: thread t handles (head t / (DH + 2), entry t % (DH + 2)),
   // entries DH and DH + 1 being the maximum and the sum.
-  for (int t = tid; t < GROUP * (DH + 2); t += kDecThreads) {
+  for (int t = tid; t < GROUP * (DH + 2); t += NT) {
     const int i = t / (DH + 2), d = t % (DH + 2);
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, red[w][i][DH]);
-    float val = mx;
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w][i][DH]);
+    float val = mx, lt = 0.0f;
     if (d != DH) {
       val = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float mw = red[w][i][DH];
         const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mx);
         val += red[w][i][d] * f;
+        if (FINAL) lt += red[w][i][DH + 1] * f;
+      }
+    } else if (FINAL) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = red[w][i][DH];
+        lt += mw == -INFINITY ? 0.0f : red[w][i][DH + 1] * __builtin_amdgcn_exp2f(mw - mx);
       }
     }
-    const int64_t slot = ((int64_t)b * a.hq + kvh * GROUP + i) * a.nsplit + split;
-    if (d < DH)
-      a.part_o[slot * DH + d] = val;
-    else
-      a.part_ml[slot * 2 + (d - DH)] = val;
+    const int h = kvh * GROUP + i;
+    if (FINAL) {
+      if (d < DH) {
+        const float ov = lt > 0.0f ? val / lt : 0.0f;
+        const int64_t oi = ((int64_t)b * a.hq + h) * DH + d;
+        if constexpr (sizeof(T) == 2)
+          reinterpret_cast<__bf16*>(a.o)[oi] = (__bf16)ov;
+        else
+          reinterpret_cast<float*>(a.o)[oi] = ov;
+      } else if (d == DH && a.lse) {
+        a.lse[(int64_t)b * a.hq + h] = lt > 0.0f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
+      }
+    } else {
+      const int64_t slot = ((int64_t)b * a.hq + h) * a.nsplit + split;
+      if (d < DH)
+        a.part_o[slot * DH + d] = val;
+      else
+        a.part_ml[slot * 2 + (d - DH)] = val;
+    }
   }
 }
 
@@ -322,19 +358,30 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(DecArgs a) {
 }
 
 template <typename T, int DH, int GROUP>
-void launch_group(const DecArgs& a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, DH, GROUP, 2>), dim3(a.nsplit, a.hkv, batch), dim3(kDecThreads), 0,
-                     stream, a);
+void launch_group(DecArgs a, int batch, int64_t max_seqlen, hipStream_t stream) {
+  if constexpr (GROUP <= 2) {  // 16 waves of this kernel fit the registers only for 1-2 heads per KV head
+    if ((int64_t)batch * a.hkv >= 256) {
+      // Enough (sequence, KV head) pairs to fill the chip with one 16-wave
+      // workgroup each: no key split, no combine pass.
+      a.split = (int)(max_seqlen > 0 ? max_seqlen : 1);
+      a.nsplit = 1;
+      hipLaunchKernelGGL((decode_split_kernel<T, DH, GROUP, 2, 16, true>), dim3(1, a.hkv, batch), dim3(1024), 0,
+                         stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_split_kernel<T, DH, GROUP, 2, kDecWaves, false>), dim3(a.nsplit, a.hkv, batch),
+                     dim3(kDecThreads), 0, stream, a);
   hipLaunchKernelGGL((decode_combine_kernel<T, DH>), dim3(a.hq, batch), dim3(DH), 0, stream, a);
 }
 
 template <typename T, int DH>
-hipError_t launch_dh(const DecArgs& a, int batch, hipStream_t stream) {
+hipError_t launch_dh(const DecArgs& a, int batch, int64_t max_seqlen, hipStream_t stream) {
   switch (a.hq / a.hkv) {
-    case 1: launch_group<T, DH, 1>(a, batch, stream); break;
-    case 2: launch_group<T, DH, 2>(a, batch, stream); break;
-    case 4: launch_group<T, DH, 4>(a, batch, stream); break;
-    case 8: launch_group<T, DH, 8>(a, batch, stream); break;
+    case 1: launch_group<T, DH, 1>(a, batch, max_seqlen, stream); break;
+    case 2: launch_group<T, DH, 2>(a, batch, max_seqlen, stream); break;
+    case 4: launch_group<T, DH, 4>(a, batch, max_seqlen, stream); break;
+    case 8: launch_group<T, DH, 8>(a, batch, max_seqlen, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -364,8 +411,10 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
   a.part_ml = workspace + (int64_t)batch * hq * a.nsplit * dh;
   a.scale_log2 = scale * kLog2e;
   if (elem_bytes == 2)
-    return dh == 128 ? launch_dh<uint16_t, 128>(a, batch, stream) : launch_dh<uint16_t, 64>(a, batch, stream);
-  return dh == 128 ? launch_dh<float, 128>(a, batch, stream) : launch_dh<float, 64>(a, batch, stream);
+    return dh == 128 ? launch_dh<uint16_t, 128>(a, batch, max_seqlen, stream)
+                     : launch_dh<uint16_t, 64>(a, batch, max_seqlen, stream);
+  return dh == 128 ? launch_dh<float, 128>(a, batch, max_seqlen, stream)
+                   : launch_dh<float, 64>(a, batch, max_seqlen, stream);
 }
 
 }  // namespace tg

@@ -503,6 +503,9 @@ def _decode_case(tg, lens, hq, hkv, dh, dtype, seed, gkind="uniform", gain=False
     (torch.bfloat16, [4096 + 37] * 3, 16, 16, 64, "uniform", True),
     (torch.float32, [5, 300, 1025], 4, 4, 128, None, False),
     (torch.float32, [0, 2, 777], 8, 2, 64, "wide", True),
+    # (sequence, KV head) pairs >= 256 with 1-2 heads per KV head: one block per pair, no combine pass
+    (torch.bfloat16, [0, 1, 300, 64, 1000, 5, 129, 2] * 4, 8, 8, 64, "uniform", True),
+    (torch.float32, [700, 0, 65, 1] * 4, 32, 16, 128, None, False),
 ])
 def test_decode_parity(gpu_lib, dtype, lens, hq, hkv, dh, gkind, gain):
     _say("decode", dtype, lens, hq, hkv, dh, gkind, gain)
