@@ -36,10 +36,11 @@
 // attn_bf16_kernel (streaming bias): a workgroup owns a pair of query tiles,
 // (T-1-p) then p, so every workgroup has the same causal work; each step
 // copies the next key tile and its bias and positions, computes, then waits.
-// attn_bf16_pp_kernel (ping-pong): one query tile per workgroup, longest
-// first; the two groups alternate MFMA and VALU slots so that the two waves
-// of a SIMD overlap matrix and vector work, with copies issued three slots
-// ahead (see the kernel's own comment).
+// attn_bf16_pp_kernel (ping-pong): the same tile pairs, with the bias of
+// every visible key in one LDS table built once per pair; the two groups
+// alternate MFMA and VALU slots so that the two waves of a SIMD overlap
+// matrix and vector work, with copies issued three slots ahead (see the
+// kernel's own comment).
 #include <cmath>
 
 #include "tg_internal.h"
@@ -416,12 +417,10 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
-  // One 128-query tile per workgroup, tiles in decreasing order of causal
-  // work (all heads of the last tile first).  The first wave of workgroups
-  // fills the chip with the long tiles and each CU that finishes takes the
-  // next shorter one, which pairs long and short tiles per CU without a loop
-  // over two tiles.  rr = blockIdx % hq runs over the KV heads first, so all
-  // query heads of a KV head land on one XCD and share its K/V in L2.
+  // Two 128-query tiles per workgroup: workgroup p takes tile T-1-p, then
+  // tile p, so every workgroup does the same causal work (T tiles of keys).
+  // rr = blockIdx % hq runs over the KV heads first, so all query heads of a
+  // KV head land on one XCD and share its K/V in L2.
   const int hq = a.hq, hkv = a.hkv, group = hq / hkv;
   const int rr = blockIdx.x % hq;
   const int kvh = rr % hkv;
@@ -433,8 +432,13 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     L = a.cu[blockIdx.y + 1] - (int)s0;
   }
   const int ntiles = (L + C::BM - 1) / C::BM;
-  const int mt = ntiles - 1 - (int)(blockIdx.x / hq);
-  if (mt < 0) return;
+  // The short tile's keys are a prefix of the long tile's, so the bias table
+  // built for the long tile serves both.  The tile body is a lambda called
+  // twice rather than a loop: a loop keeps its values live across the back
+  // edge and spills.
+  const int pair = (int)(blockIdx.x / hq);
+  auto tile_body = [&](const int mt, const bool pass0) __attribute__((always_inline)) {
+  const int pass = pass0 ? 0 : 1;
 
   const uint8_t* kbase = a.k + ((s0 * hkv + kvh) * DH) * 2;
   const uint8_t* vbase = a.v + ((s0 * hkv + kvh) * DH) * 2;
@@ -507,8 +511,10 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   // values unused): a NULL test inside the loop would split the loads into
   // branches that each wait for their own load.
   const float* gsrc = has_gate ? a.g + s0 : reinterpret_cast<const float*>(a.pos + s0);
+  if (pass == 0) {
 #pragma unroll
-  for (int i = 0; i < GPT; ++i) gv[i] = gsrc[min(tid + 512 * i, L - 1)];
+    for (int i = 0; i < GPT; ++i) gv[i] = gsrc[min(tid + 512 * i, L - 1)];
+  }
   // Copies per wave in batch b (K of tile b+2, V of tile b+1); here go batch
   // -2 (K(0)) and batch -1 (K(1), V(0)).
   if (0 < niter) issue(kbase, off_k, grp, k_addr[0]);
@@ -523,8 +529,8 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     else
       wait_vm<0>();
   }
-  if (!has_gate && tid < BN) bias_all[tid] = 0.0f;
-  if (a.g) {
+  if (pass == 0 && !has_gate && tid < BN) bias_all[tid] = 0.0f;
+  if (pass == 0 && a.g) {
     const float inv_c = gain / c;  // gate bias times the head's gain
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
@@ -770,6 +776,13 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       }
     }
   }
+  };
+  const int mt0 = ntiles - 1 - pair;
+  if (pair >= (ntiles + 1) / 2) return;  // pairs past this prompt's tiles
+  tile_body(mt0, true);
+  if (pair >= mt0) return;
+  __syncthreads();  // the next tile's copies reuse the LDS of this tile's merge
+  tile_body(pair, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -877,19 +890,18 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   const int64_t npairs = (ntiles + 1) / 2;
   const dim3 grid((unsigned)(npairs * hq), cu_seqlens ? (unsigned)batch : 1u);
   // The ping-pong kernel keeps a bias entry per key (rounded up to a 64-key
-  // tile) in LDS and takes one query tile per workgroup; without a gate it
-  // needs no table and takes any length.  Longer gated prompts take the
-  // streaming-bias kernel, two tiles per workgroup.
+  // tile) in LDS; without a gate it needs no table and takes any length.
+  // Longer gated prompts take the streaming-bias kernel.  Both take the
+  // same grid of tile pairs.
   const int64_t keys = (max_seqlen + 63) / 64 * 64;
-  const dim3 grid_pp((unsigned)(ntiles * hq), cu_seqlens ? (unsigned)batch : 1u);
   if (dh == 128) {
     if (!g || keys <= PPCfg<128>::MAXK)
-      hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, grid_pp, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, grid, dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
   } else {
     if (!g || keys <= PPCfg<64>::MAXK)
-      hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, grid_pp, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, grid, dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
   }
