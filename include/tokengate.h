@@ -38,6 +38,10 @@
  *  - Gate values g are fp32.  Indices and positions are int32.
  *  - A packed ragged batch (cu_seqlens) holds at most 65535 prompts per call
  *    (one launch-grid row per prompt); larger batches give TG_ERR_UNSUPPORTED.
+ *  - A call whose launch grid would exceed what one dispatch can count (2^32
+ *    work-items in x, 65535 workgroups in y and z) returns TG_ERR_UNSUPPORTED
+ *    before any HIP call: for example a gather or rope_kv over 2^26 or 2^24
+ *    rows, or a select over 2^22 prompts.  Split such work over several calls.
  *  - Later rows beside the prefill path: decode attention over the compact
  *    cache (tg_decode_attn, the only call that takes a caller workspace), the
  *    upper layers' dense products (tg_qkv_proj, tg_linear, tg_swiglu) and a

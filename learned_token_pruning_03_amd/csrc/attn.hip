@@ -888,6 +888,7 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   a.scale_log2 = scale * kLog2e;
   const int64_t ntiles = (max_seqlen + 127) / 128;
   const int64_t npairs = (ntiles + 1) / 2;
+  if (!grid_fits(npairs * hq, 512, cu_seqlens ? batch : 1)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(npairs * hq), cu_seqlens ? (unsigned)batch : 1u);
   // The ping-pong kernel keeps a bias entry per key (rounded up to a 64-key
   // tile) in LDS; without a gate it needs no table and takes any length.
@@ -912,6 +913,7 @@ hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch, 
                            int hq, int hkv, int dh, float scale, const float* q, const float* k,
                            const float* v, const float* g, const float* head_gain, const int32_t* pos,
                            float* o, float* lse, hipStream_t stream) {
+  if (!grid_fits((max_seqlen + 63) / 64, 64, hq, cu_seqlens ? batch : 1)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((max_seqlen + 63) / 64), (unsigned)hq, cu_seqlens ? (unsigned)batch : 1u);
   if (dh == 128)
     hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos, o,

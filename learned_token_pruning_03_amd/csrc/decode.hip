@@ -408,6 +408,9 @@ hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, i
   a.split = decode_split_keys(batch, hkv, max_seqlen);
   a.nsplit = (int)((max_seqlen + a.split - 1) / a.split);
   if (a.nsplit < 1) a.nsplit = 1;
+  // Split blocks over (split, KV head, sequence), combine blocks over (query head, sequence).
+  if (!grid_fits(a.nsplit, kDecThreads, hkv, batch) || !grid_fits(hq, dh, batch))
+    return hipErrorInvalidConfiguration;
   a.part_ml = workspace + (int64_t)batch * hq * a.nsplit * dh;
   a.scale_log2 = scale * kLog2e;
   if (elem_bytes == 2)

@@ -257,8 +257,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs p) {
 
 template <int BM, int EPI>
 hipError_t launch_bm(GemmArgs p, hipStream_t stream) {
-  p.tiles_m = (p.m + BM - 1) / BM;
+  p.tiles_m = (int)(((int64_t)p.m + BM - 1) / BM);
   p.tiles_n = p.n / (EPI == kEpiSwiglu ? kGemmBN / 2 : kGemmBN);
+  if (!grid_fits((int64_t)p.tiles_m * p.tiles_n, kGemmThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, EPI>), dim3(p.tiles_m * p.tiles_n), dim3(kGemmThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -303,6 +303,7 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
 hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
                             const void* w1, const float* b1, const float* w2, float b2, float* g,
                             float* s, hipStream_t stream) {
+  if (!grid_fits((n + kGateBM - 1) / kGateBM, kGateThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n + kGateBM - 1) / kGateBM));
   const auto* hh = static_cast<const uint16_t*>(h);
   const auto* ww = static_cast<const uint16_t*>(w1);
@@ -326,6 +327,7 @@ hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t
 hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,
                            const float* w1, const float* b1, const float* w2, float b2, float* g,
                            float* s, hipStream_t stream) {
+  if (!grid_fits((n + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n + 3) / 4));
   hipLaunchKernelGGL(gate_f32_kernel, grid, dim3(256), 0, stream, h, ld_h, (int)n, d, hidden, w1, b1,
                      w2, b2, g, s);

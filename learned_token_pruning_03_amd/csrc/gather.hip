@@ -66,6 +66,8 @@ hipError_t launch_gather(int elem_bytes, int64_t n, int64_t n_kept, int d, const
                          int batch, int64_t max_kept, hipStream_t stream) {
   const int row_chunks = (int)((int64_t)d * elem_bytes / 16);
   const int64_t rows = cu_kept ? max_kept : n_kept;
+  if (!grid_fits((rows + kRowsPerBlock - 1) / kRowsPerBlock, 256, cu_kept ? batch : 1))
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), cu_kept ? (unsigned)batch : 1u);
   hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, stream, n, n_kept, row_chunks, idx,
                      static_cast<const uint8_t*>(h), ld_h * elem_bytes, g,
@@ -109,6 +111,7 @@ __global__ __launch_bounds__(256) void check_pos_kernel(const int32_t* __restric
 
 hipError_t launch_check_positions(const int32_t* pos, int64_t total, const int32_t* cu_seqlens, int batch,
                                    int32_t* first_bad, hipStream_t stream) {
+  if (!grid_fits((total + 255) / 256, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(check_pos_init_kernel, dim3(1), dim3(64), 0, stream, first_bad, (int32_t)total);
   if (total > 0)
     hipLaunchKernelGGL(check_pos_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, pos,

@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(int hq, int hkv, int dh,
 hipError_t launch_rope_table(float* cos_sin, int64_t max_pos, int dh, double base,
                              hipStream_t stream) {
   const int64_t total = max_pos * (dh / 2);
+  if (!grid_fits((total + 255) / 256, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
                      cos_sin, max_pos, dh, base);
   return hipGetLastError();
@@ -147,6 +148,7 @@ hipError_t launch_rope_table(float* cos_sin, int64_t max_pos, int dh, double bas
 hipError_t launch_rope_kv(int elem_bytes, int64_t n_kept, int hq, int hkv, int dh, const int32_t* pos,
                           const float* cos_sin, int64_t max_pos, void* q, const void* k, const void* v,
                           void* k_cache, void* v_cache, hipStream_t stream) {
+  if (!grid_fits(n_kept, 256)) return hipErrorInvalidConfiguration;
   auto* qb = static_cast<uint8_t*>(q);
   auto* kb = static_cast<const uint8_t*>(k);
   auto* vb = static_cast<const uint8_t*>(v);

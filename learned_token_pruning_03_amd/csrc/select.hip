@@ -303,6 +303,7 @@ void launch_kpt(const float* g, int n, int64_t k, int q, const int32_t* cu, cons
 hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len, const int32_t* cu_seqlens,
                          const int32_t* q_lens, int batch, int64_t max_seqlen, int32_t* idx,
                          int32_t* cu_kept, hipStream_t stream) {
+  if (!grid_fits(batch, kSelThreads)) return hipErrorInvalidConfiguration;
   // Smallest register footprint that holds the longest prompt; longer
   // prompts stream their keys through the same registers once per pass.
   const int64_t m = max_seqlen;

@@ -26,6 +26,8 @@ tg_status ok() {
 }
 
 tg_status from_hip(hipError_t e, const char* what) {
+  if (e == hipErrorInvalidConfiguration)  // refused by a launcher before any HIP call
+    return fail(TG_ERR_UNSUPPORTED, "%s: launch grid beyond 2^32 work-items in x or 65535 blocks in y, z", what);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {
     return fail(TG_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
@@ -334,7 +336,7 @@ static tg_status check_dense(const char* what, tg_dtype dtype, int64_t m, int64_
                              const void* x, int64_t ld_x, const void* w, int64_t ld_w, void* y, int64_t ld_y) {
   if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
   if (dtype != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "%s: only TG_BF16 is implemented", what);
-  if (m < 0 || m > kMaxI32 || n <= 0 || k <= 0)
+  if (m < 0 || m > kMaxI32 - 256 || n <= 0 || k <= 0)
     return fail(TG_ERR_INVALID_ARG, "%s: m=%lld, n=%lld, k=%lld out of range", what, (long long)m, (long long)n,
                 (long long)k);
   if (n % n_mult != 0 || k % 32 != 0)

@@ -70,6 +70,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One dispatch counts work-items in 32 bits in x and allows 65535 blocks in
+// y and z.  Launchers refuse larger grids before any HIP call with
+// hipErrorInvalidConfiguration, which the C ABI reports as TG_ERR_UNSUPPORTED.
+constexpr int64_t kMaxGridItemsX = 0xffffffffLL;
+constexpr int64_t kMaxGridBlocksYZ = 65535;
+inline bool grid_fits(int64_t blocks_x, int threads, int64_t y = 1, int64_t z = 1) {
+  return blocks_x >= 0 && blocks_x <= kMaxGridItemsX / threads && y >= 0 && y <= kMaxGridBlocksYZ && z >= 0 &&
+         z <= kMaxGridBlocksYZ;
+}
+
 // ---- launchers (defined in the kernel translation units) -------------------
 hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
                             const void* w1, const float* b1, const float* w2, float b2,

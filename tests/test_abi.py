@@ -186,3 +186,31 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         tg.tg_select_topk(torch.zeros(10), 5, 1)
+
+
+def test_grids_beyond_one_dispatch_are_refused_before_any_hip_call(lib):
+    """A dispatch counts work-items in 32 bits in x and 65535 workgroups in y and
+    z; sizes that fit in memory can still exceed that, and must be refused on the
+    host (TG_ERR_UNSUPPORTED), not launched with a truncated grid."""
+    U = tg.TG_ERR_UNSUPPORTED
+    # gather: one wave per row, 2^26 rows of 16 bytes (1 GiB) -> 2^32 work-items
+    assert lib.tg_gather(tg.TG_BF16, 1 << 27, 1 << 26, 8, FAKE, FAKE, 8, None, FAKE, None, None, None) == U
+    assert b"launch grid" in lib.tg_last_error()
+    # rope_kv: one 256-thread workgroup per kept token
+    assert lib.tg_rope_kv(tg.TG_BF16, 1 << 24, 1, 1, 16, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == U
+    # rope_table: one work-item per (position, frequency)
+    assert lib.tg_rope_table(FAKE, 1 << 26, 128, 10000.0, None) == U
+    # fp32 gate: four rows per 256-thread workgroup
+    assert lib.tg_gate_score(tg.TG_FP32, 1 << 26, 4, 4, FAKE, 4, FAKE, None, FAKE, 0.0, FAKE, None, None) == U
+    # ragged select: one 1024-thread workgroup per prompt
+    assert lib.tg_select_topk_varlen(FAKE, FAKE, FAKE, 1 << 22, 1, 1, FAKE, FAKE, None) == U
+    # fp32 attention: query heads index the grid's y dimension
+    assert lib.tg_gated_attn(tg.TG_FP32, 16, 70000, 70000, 64, 0.1, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                             None) == U
+    # decode: KV heads index the grid's y dimension
+    ws = lib.tg_decode_attn_workspace_size(1, 64, 70000, 70000, 64)
+    assert ws > 0
+    assert lib.tg_decode_attn(tg.TG_BF16, FAKE, 1, 64, 70000, 70000, 64, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
+                              None, FAKE, ws, None) == U
+    # the same gather with nothing to copy is a no-op, not a refusal
+    assert lib.tg_gather(tg.TG_BF16, 1 << 27, 0, 8, FAKE, FAKE, 8, None, FAKE, None, None, None) == tg.TG_OK
