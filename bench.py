@@ -45,6 +45,9 @@ def parse_args(argv=None):
     p.add_argument("--no-decode", action="store_true",
                    help="skip the decode attention figure over compact KV caches")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
+    p.add_argument("--select", default="auto", choices=["auto", "one", "ws"],
+                   help="top-K entry point: tg_select_topk (one workgroup per prompt), tg_select_topk_ws "
+                        "(several workgroups, caller workspace), or auto: ws from %d tokens" % SELECT_WS_FROM)
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the run, launch a plain 1 GiB -> 1 GiB streaming kernel (torch.neg on fp32) "
                         "three times; its PMC byte counters calibrate FETCH_SIZE / WRITE_SIZE")
@@ -59,10 +62,16 @@ def _file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+# The multi-workgroup select costs a fixed ~27 us (six short kernels) where the
+# one-workgroup kernel grows with the prompt: 21 us at 16k tokens, 32 us at
+# 32k, 114 us at 128k (events, one MI355X).
+SELECT_WS_FROM = 24576
+
+
 class Path:
     """Device buffers and the launch sequence of one workload."""
 
-    def __init__(self, tg, W, name, dev):
+    def __init__(self, tg, W, name, dev, select="auto"):
         import torch
         sh = W.SHAPES[name]
         seed = W.SEEDS[name]
@@ -82,6 +91,9 @@ class Path:
         f32, i32 = torch.float32, torch.int32
         self.g = torch.empty(sh.n, dtype=f32, device=dev)
         self.idx = torch.empty(kept, dtype=i32, device=dev)
+        self.select_ws = select == "ws" or (select == "auto" and sh.n >= SELECT_WS_FROM)
+        self.sel_workspace = (torch.empty(tg.tg_select_topk_workspace_size(sh.n), dtype=torch.uint8, device=dev)
+                              if self.select_ws else None)
         self.hk = torch.empty(kept, sh.d, dtype=sh.dtype, device=dev)
         self.gk = torch.empty(kept, dtype=f32, device=dev)
         self.pos = torch.empty(kept, dtype=i32, device=dev)
@@ -99,7 +111,10 @@ class Path:
 
     def select(self):
         g = self.g if self.wide_g is None else self.wide_g
-        self.tg.tg_select_topk(g, self.sh.k, self.sh.q_len, idx=self.idx)
+        if self.select_ws:
+            self.tg.tg_select_topk_ws(g, self.sh.k, self.sh.q_len, idx=self.idx, workspace=self.sel_workspace)
+        else:
+            self.tg.tg_select_topk(g, self.sh.k, self.sh.q_len, idx=self.idx)
 
     def gather(self):
         g = self.g if self.wide_g is None else self.wide_g
@@ -498,7 +513,7 @@ def main(argv=None):
     tg.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    path = Path(tg, W, args.workload, dev)
+    path = Path(tg, W, args.workload, dev, select=args.select)
     sh = path.sh
     print(f"[bench] workload {args.workload}: N={sh.n} K={sh.k} layers={sh.layers}", file=sys.stderr, flush=True)
 
@@ -603,6 +618,7 @@ def main(argv=None):
                    "upper_layers": sh.layers, "global_batch": 1, "seq_len": sh.n},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "select_entry": "tg_select_topk_ws" if path.select_ws else "tg_select_topk",
         "stages": stages,
         "hip_graph": graph,
         "full_context": full,

@@ -43,7 +43,8 @@
  *    before any HIP call: for example a gather or rope_kv over 2^26 or 2^24
  *    rows, or a select over 2^22 prompts.  Split such work over several calls.
  *  - Later rows beside the prefill path: decode attention over the compact
- *    cache (tg_decode_attn, the only call that takes a caller workspace), the
+ *    cache (tg_decode_attn, which takes a caller workspace, as does the
+ *    multi-workgroup select tg_select_topk_ws), the
  *    upper layers' dense products (tg_qkv_proj, tg_linear, tg_swiglu) and a
  *    device-side check of the position order (tg_check_positions).
  */
@@ -133,6 +134,21 @@ TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hid
  * ------------------------------------------------------------------------- */
 TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_len,
                                 int32_t* idx, hipStream_t stream);
+
+/* The same selection (same arguments, same output, bit for bit) spread over
+ * ceil((n - q_len) / 2048) workgroups, for prompts long enough that one
+ * workgroup's radix passes dominate the path.  It takes a caller workspace of
+ * at least tg_select_topk_workspace_size(n) bytes, 16-byte aligned, whose
+ * contents need not be initialised (the call clears what it uses); calls that
+ * share a workspace must be ordered on one stream.  Budgets that keep the
+ * whole document or none of it, and documents above 2^24 tokens, run the
+ * one-workgroup kernel of tg_select_topk instead.
+ * Errors: as tg_select_topk; a NULL, misaligned or too small workspace ->
+ * INVALID_ARG. */
+TG_API int64_t tg_select_topk_workspace_size(int64_t n); /* -1 for n outside [0, 2^31) */
+TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t q_len,
+                                   int32_t* idx, void* workspace, int64_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* Ragged batch of prompts packed along the token axis.
  *   g           [total] fp32, prompt b occupies [cu_seqlens[b], cu_seqlens[b+1]).

@@ -31,5 +31,7 @@ from .binding import (  # noqa: F401
     tg_rope_table,
     tg_select_topk,
     tg_select_topk_varlen,
+    tg_select_topk_workspace_size,
+    tg_select_topk_ws,
     tg_swiglu,
 )

@@ -35,6 +35,8 @@ SIGNATURES = {
     "tg_gate_score": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32,
                        _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_select_topk": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
+    "tg_select_topk_workspace_size": ([_c_i64], _c_i64),
+    "tg_select_topk_ws": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
     "tg_select_topk_varlen": ([_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
                               ctypes.c_int),
     "tg_gather": ([ctypes.c_int, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -151,6 +153,31 @@ def tg_select_topk(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tens
         idx = torch.empty(kept, dtype=torch.int32, device=g.device)
     _need(idx.numel() >= kept and idx.dtype == torch.int32, "idx must be int32 with min(k, n) entries")
     _check("tg_select_topk", lib.tg_select_topk(_ptr(g), n, int(k), int(q_len), _ptr(idx), _stream(g)))
+    return idx
+
+
+def tg_select_topk_workspace_size(n: int) -> int:
+    size = load_library().tg_select_topk_workspace_size(int(n))
+    _need(size >= 0, "invalid select size")
+    return size
+
+
+def tg_select_topk_ws(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """tg_select_topk spread over several workgroups, with a caller workspace."""
+    lib = load_library()
+    _need(g.dim() == 1 and g.dtype == torch.float32 and g.is_contiguous(), "g must be contiguous fp32 [n]")
+    n = g.shape[0]
+    kept = min(int(k), n)
+    if idx is None:
+        idx = torch.empty(kept, dtype=torch.int32, device=g.device)
+    _need(idx.numel() >= kept and idx.dtype == torch.int32, "idx must be int32 with min(k, n) entries")
+    need = tg_select_topk_workspace_size(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=g.device)
+    _check("tg_select_topk_ws",
+           lib.tg_select_topk_ws(_ptr(g), n, int(k), int(q_len), _ptr(idx), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(g)))
     return idx
 
 

@@ -108,6 +108,29 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
                   "select");
 }
 
+TG_API int64_t tg_select_topk_workspace_size(int64_t n) {
+  if (n < 0 || n > kMaxI32) return -1;
+  return tg::select_mw_workspace_bytes(n);
+}
+
+TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx,
+                                   void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (n < 0 || n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "select_ws: n=%lld out of range", (long long)n);
+  if (k < 0) return fail(TG_ERR_INVALID_ARG, "select_ws: k=%lld < 0", (long long)k);
+  const int64_t kept = k < n ? k : n;
+  if (q_len < 0 || q_len > kept)
+    return fail(TG_ERR_INVALID_ARG, "select_ws: q_len=%lld outside [0, min(k, n)=%lld]", (long long)q_len,
+                (long long)kept);
+  if (n == 0) return ok();
+  if (!g || !idx || !workspace) return fail(TG_ERR_INVALID_ARG, "select_ws: NULL g, idx or workspace");
+  if (!aligned16(workspace)) return fail(TG_ERR_INVALID_ARG, "select_ws: workspace must be 16-byte aligned");
+  const int64_t need = tg::select_mw_workspace_bytes(n);
+  if (workspace_bytes < need)
+    return fail(TG_ERR_INVALID_ARG, "select_ws: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  return from_hip(tg::launch_select_mw(g, n, k, q_len, idx, workspace, stream), "select_ws");
+}
+
 TG_API tg_status tg_select_topk_varlen(const float* g, const int32_t* cu_seqlens,
                                        const int32_t* q_lens, int32_t batch, int64_t max_seqlen,
                                        int64_t k, int32_t* idx_local, int32_t* cu_kept,

@@ -88,6 +88,12 @@ hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t
                            const float* w1, const float* b1, const float* w2, float b2,
                            float* g, float* s, hipStream_t stream);
 
+// Several workgroups per prompt (select.hip); prompts above kSelectMwMaxN
+// document tokens, and the degenerate budgets, go to the one-workgroup kernel.
+constexpr int64_t kSelectMwMaxN = int64_t(1) << 24;
+int64_t select_mw_workspace_bytes(int64_t n);
+hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, void* workspace,
+                            hipStream_t stream);
 hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len,
                          const int32_t* cu_seqlens, const int32_t* q_lens, int batch,
                          int64_t max_seqlen, int32_t* idx, int32_t* cu_kept,

@@ -24,7 +24,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
-    for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_gather", "tg_gather_varlen",
+    for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
+                 "tg_select_topk_ws", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
                  "tg_linear", "tg_swiglu", "tg_qkv_proj", "tg_check_positions",
@@ -214,3 +215,15 @@ def test_grids_beyond_one_dispatch_are_refused_before_any_hip_call(lib):
                               None, FAKE, ws, None) == U
     # the same gather with nothing to copy is a no-op, not a refusal
     assert lib.tg_gather(tg.TG_BF16, 1 << 27, 0, 8, FAKE, FAKE, 8, None, FAKE, None, None, None) == tg.TG_OK
+
+
+def test_select_ws_validation_without_a_gpu(lib):
+    ws = lib.tg_select_topk_workspace_size(32768)
+    assert ws >= (2048 + 2048 + 1024 + 16 * 2) * 4  # three histograms, two counts per 2048-key chunk
+    assert lib.tg_select_topk_workspace_size(-1) == -1
+    ok = tg.TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == ok  # too small
+    assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, None, ws, None) == ok  # NULL workspace
+    assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE + 4, ws, None) == ok  # misaligned
+    assert lib.tg_select_topk_ws(FAKE, 32768, 10, 11, FAKE, FAKE, ws, None) == ok  # q_len > budget
+    assert lib.tg_select_topk_ws(FAKE, 0, 10, 0, FAKE, None, 0, None) == tg.TG_OK  # empty: no-op

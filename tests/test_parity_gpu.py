@@ -76,8 +76,11 @@ def test_gate_fp32_ragged(gpu_lib):
 
 
 # ----------------------------------------------------------------------------- select
-def _sel(tg, g_cpu, k, q):
-    idx = tg.tg_select_topk(g_cpu.to(DEV), k, q)
+def _sel(tg, g_cpu, k, q, entry="one"):
+    """entry "one": tg_select_topk (one workgroup per prompt); "ws": tg_select_topk_ws
+    (several workgroups, caller workspace)."""
+    g = g_cpu.to(DEV)
+    idx = tg.tg_select_topk(g, k, q) if entry == "one" else tg.tg_select_topk_ws(g, k, q)
     torch.cuda.synchronize()
     return idx.cpu().numpy().astype(np.int64)
 
@@ -106,12 +109,13 @@ def _score_vector(kind, n, seed):
     raise ValueError(kind)
 
 
+@pytest.mark.parametrize("entry", ["one", "ws"])
 @pytest.mark.parametrize("kind", ["uniform", "wide", "tie8", "equal", "saturated", "special"])
 @pytest.mark.parametrize("n,k,q", [(512, 128, 32), (1000, 300, 17), (5000, 999, 0), (4097, 4096, 64),
-                                   (70, 64, 64), (64, 100, 10), (3, 2, 1)])
-def test_select_bit_exact(gpu_lib, kind, n, k, q):
+                                   (70, 64, 64), (64, 100, 10), (3, 2, 1), (2049, 5, 1), (20001, 7000, 5)])
+def test_select_bit_exact(gpu_lib, kind, n, k, q, entry):
     g = _score_vector(kind, n, n + k)
-    got = _sel(gpu_lib, g, k, q)
+    got = _sel(gpu_lib, g, k, q, entry)
     want = ref_select(g.numpy(), k, q)
     np.testing.assert_array_equal(got, want)
 
@@ -122,17 +126,38 @@ def test_select_bit_exact(gpu_lib, kind, n, k, q):
                                              ("qwen1p7b_128k", 131072, 8192, 64, "wide"),
                                              ("qwen1p7b_128k", 131072, 8192, 64, "tie8"),
                                              ("long", 200003, 20000, 100, "uniform")])
-def test_select_full_sizes(gpu_lib, name, n, k, q, kind):
-    _say("select", name, n, k, q, kind)
+@pytest.mark.parametrize("entry", ["one", "ws"])
+def test_select_full_sizes(gpu_lib, name, n, k, q, kind, entry):
+    _say("select", entry, name, n, k, q, kind)
     g = _score_vector(kind, n, 3)
-    np.testing.assert_array_equal(_sel(gpu_lib, g, k, q), ref_select(g.numpy(), k, q))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, k, q, entry), ref_select(g.numpy(), k, q))
 
 
-def test_select_budget_covers_prompt_and_tail_only(gpu_lib):
+@pytest.mark.parametrize("entry", ["one", "ws"])
+def test_select_budget_covers_prompt_and_tail_only(gpu_lib, entry):
     g = W.random_scores(300, 1)
-    np.testing.assert_array_equal(_sel(gpu_lib, g, 300, 20), np.arange(300))
-    np.testing.assert_array_equal(_sel(gpu_lib, g, 1000, 20), np.arange(300))
-    np.testing.assert_array_equal(_sel(gpu_lib, g, 20, 20), np.arange(280, 300))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 300, 20, entry), np.arange(300))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 1000, 20, entry), np.arange(300))
+    np.testing.assert_array_equal(_sel(gpu_lib, g, 20, 20, entry), np.arange(280, 300))
+
+
+def test_select_ws_dirty_workspace_and_unaligned_scores(gpu_lib):
+    """The multi-workgroup select clears what it uses: a workspace full of garbage, or
+    left over from a longer call, gives the same answer; scores that start off a
+    16-byte boundary take the scalar loads."""
+    _say("select ws dirty workspace")
+    n_big = 40000
+    ws = torch.full((gpu_lib.tg_select_topk_workspace_size(n_big),), 0xAB, dtype=torch.uint8, device=DEV)
+    for n, k, q, kind, seed in [(40000, 5000, 64, "wide", 1), (9000, 1000, 8, "tie8", 2), (40000, 5000, 64, "uniform", 3)]:
+        g = _score_vector(kind, n, seed)
+        idx = gpu_lib.tg_select_topk_ws(g.to(DEV), k, q, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_select(g.numpy(), k, q))
+    base = _score_vector("uniform", 30001, 4)
+    gd = base.to(DEV)[1:]  # 4-byte offset from the allocation
+    idx = gpu_lib.tg_select_topk_ws(gd, 3000, 16, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_select(base[1:].numpy(), 3000, 16))
 
 
 def test_select_varlen_ragged_batch(gpu_lib):
@@ -697,9 +722,11 @@ def test_path_replayed_from_a_hip_graph(gpu_lib):
     table = tg.tg_rope_table(n, dh, 1e6, DEV)
     cu = torch.tensor([0, k], dtype=torch.int32, device=DEV)
     ws = torch.empty(tg.tg_decode_attn_workspace_size(1, k, hq, hkv, dh), dtype=torch.uint8, device=DEV)
+    sws = torch.empty(tg.tg_select_topk_workspace_size(n), dtype=torch.uint8, device=DEV)
 
     def buffers():
         return {"g": torch.empty(n, device=DEV), "idx": torch.empty(k, dtype=torch.int32, device=DEV),
+                "idx_ws": torch.empty(k, dtype=torch.int32, device=DEV),
                 "hk": torch.empty(k, d, dtype=torch.bfloat16, device=DEV), "gk": torch.empty(k, device=DEV),
                 "pos": torch.empty(k, dtype=torch.int32, device=DEV), "q": torch.empty_like(q0),
                 "kc": torch.empty_like(kk), "vc": torch.empty_like(vv), "o": torch.empty_like(q0),
@@ -709,6 +736,7 @@ def test_path_replayed_from_a_hip_graph(gpu_lib):
         b["q"].copy_(q0)  # RoPE rotates q in place: start every run from the same q
         tg.tg_gate_score(h, w1, b1, w2, b2, g=b["g"])
         tg.tg_select_topk(b["g"], k, q_len, idx=b["idx"])
+        tg.tg_select_topk_ws(b["g"], k, q_len, idx=b["idx_ws"], workspace=sws)  # its zero kernel, too
         tg.tg_gather(h, b["g"], b["idx"], h_out=b["hk"], g_out=b["gk"], pos_out=b["pos"])
         tg.tg_rope_kv(b["q"], kk, vv, b["pos"], table, k_cache=b["kc"], v_cache=b["vc"])
         tg.tg_gated_attn(b["q"], b["kc"], b["vc"], b["gk"], b["pos"], o=b["o"], lse=b["lse"])
@@ -718,6 +746,7 @@ def test_path_replayed_from_a_hip_graph(gpu_lib):
     path(eager)
     torch.cuda.synchronize()
     want = {name: t.clone() for name, t in eager.items()}
+    assert torch.equal(want["idx"], want["idx_ws"])
 
     graphed = buffers()
     side = torch.cuda.Stream()
