@@ -141,6 +141,21 @@ def test_select_budget_covers_prompt_and_tail_only(gpu_lib, entry):
     np.testing.assert_array_equal(_sel(gpu_lib, g, 20, 20, entry), np.arange(280, 300))
 
 
+@pytest.mark.parametrize("doc_extra", [0, 1])
+def test_select_ws_at_its_largest_document(gpu_lib, doc_extra):
+    """2^24 document tokens: the most the multi-workgroup path takes (8192 chunks,
+    each summing up to 8191 chunk counts for its offset); one token more falls back
+    to the one-workgroup kernel.  Tie-heavy scores, so the last radix pass and the
+    equal-key rule both matter."""
+    q = 64
+    n = (1 << 24) + doc_extra + q
+    _say("select ws largest document", n)
+    g = W.tie_storm_scores(n, 8, 5 + doc_extra)
+    k = (1 << 20) + q
+    got = _sel(gpu_lib, g, k, q, "ws")
+    np.testing.assert_array_equal(got, ref_select(g.numpy(), k, q))
+
+
 def test_select_ws_dirty_workspace_and_unaligned_scores(gpu_lib):
     """The multi-workgroup select clears what it uses: a workspace full of garbage, or
     left over from a longer call, gives the same answer; scores that start off a
