@@ -475,7 +475,7 @@ def traffic_summary(fetch_dir, write_dir):
     sh = SHAPES["qwen1p7b_32k"]
     algo = stage_bytes(sh)["attn"]
     rec = {
-        "kernel": "attn_bf16_pp_kernel<128>",
+        "kernel": "attn_bf16_pp_kernel<128, false>",
         "workload": "qwen1p7b_32k",
         "kernel_source_sha256_16": _file_sha(ATTN_KERNEL_SOURCE),
         "hbm_bytes_per_launch": round(fetch + write),
@@ -552,7 +552,7 @@ def main(argv=None):
     attn_tflops = fl_attn / (attn_avg_us * 1e-6) / 1e12
     traffic = load_traffic(args.workload)
     roofline = {
-        "kernel": "attn_bf16_pp_kernel<128>",
+        "kernel": "attn_bf16_pp_kernel<128, false>",
         "bound": "mfma",
         "achieved": round(attn_tflops, 1),
         "peak": PEAK_BF16_TFLOPS,

@@ -10,11 +10,11 @@
 // accumulator, so it enters the logit inside the MFMA and then takes part in
 // the running maximum and the running sum like any other part of the logit.
 //
-// Two bf16 kernels share the tile shapes and the MFMA data flow below; the
-// launcher picks attn_bf16_pp_kernel when the gate bias of every kept key fits
-// in LDS (8192 keys at head dim 128, 16384 at 64), attn_bf16_kernel beyond.
+// One bf16 kernel, attn_bf16_pp_kernel, in two forms: the gate bias of every
+// visible key in one LDS table when it fits (8192 keys at head dim 128, 16384
+// at 64, and always without a gate), else streamed tile by tile.
 //
-// Common to both (one workgroup = 512 threads = 8 waves, two per SIMD):
+// One workgroup = 512 threads = 8 waves, two per SIMD:
 //  * the two 4-wave groups split each query tile's key range (group 0 takes
 //    the even 64-key tiles, group 1 the odd ones) and merge their partial
 //    (max, sum, output) through LDS at the end of the tile;
@@ -33,14 +33,11 @@
 //    skipped on almost every tile;
 //  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
 //    the same XCD, where they share that head's K/V in L2.
-// attn_bf16_kernel (streaming bias): a workgroup owns a pair of query tiles,
-// (T-1-p) then p, so every workgroup has the same causal work; each step
-// copies the next key tile and its bias and positions, computes, then waits.
-// attn_bf16_pp_kernel (ping-pong): the same tile pairs, with the bias of
-// every visible key in one LDS table built once per pair; the two groups
-// alternate MFMA and VALU slots so that the two waves of a SIMD overlap
-// matrix and vector work, with copies issued three slots ahead (see the
-// kernel's own comment).
+//  * a workgroup owns a pair of query tiles, (T-1-p) then p, so every
+//    workgroup has the same causal work;
+//  * the two groups alternate MFMA and VALU slots so that the two waves of a
+//    SIMD overlap matrix and vector work, with copies issued three slots
+//    ahead (see the kernel's own comment).
 #include <cmath>
 
 #include "tg_internal.h"
@@ -71,12 +68,11 @@ struct AttnCfg {
   static constexpr int CPR = DH / 8;             // 16-byte chunks per K/V row
   static constexpr int ROW = DH * 2;             // LDS bytes per K or V row (XOR-swizzled chunks)
   static constexpr int K_BYTES = BN * ROW;
-  static constexpr int V_BYTES = BN * ROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES + BN * 8;  // + bias f32 + pos i32
-  static constexpr int STAGE_BYTES = 2 * STAGE;  // both groups' copy of one pipeline stage
   static constexpr int DMA = BN * CPR / 256;     // 16-byte direct loads per thread per tensor
   static constexpr int MD = DH / 32;             // 32-row blocks of O^T
-  static_assert(4 * 64 * (DH / 2) * 4 <= STAGE_BYTES, "merge scratch (O) must fit in one stage array");
+  // The merge hands over half of each wave's O^T (MD/2 blocks of 16 fp32 per
+  // lane, 4 waves) through one K buffer pair.
+  static_assert(4 * (MD / 2) * 16 * 64 * 4 <= 2 * K_BYTES, "merge scratch (O) must fit in one buffer pair");
   // Chunk c of row r is stored at chunk c ^ swz(r).  K rows are read by
   // ds_read_b128 (16 consecutive rows, one chunk), V rows by the transposing
   // read (4 consecutive rows x 4 consecutive chunks per half-wave).
@@ -86,299 +82,11 @@ struct AttnCfg {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int DH>
-__global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
-  using C = AttnCfg<DH>;
-  // The two pipeline stages are separate LDS objects, so the compiler can
-  // tell that reads of one stage never alias the direct loads into the other
-  // and does not make them wait for those loads.
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[C::STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // Wave-uniform indices live in scalar registers (readfirstlane), so branches
-  // on them are scalar branches rather than exec-masked regions.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int w4 = wave & 3;
-  const int gtid = tid & 255;
-  const int half = lane >> 5;
-  const int r32 = lane & 31;
-
-  const int hq = a.hq, hkv = a.hkv, group = hq / hkv;
-  const int rr = blockIdx.x % hq;
-  const int pair = blockIdx.x / hq;
-  const int kvh = rr % hkv;
-  const int head = kvh * group + rr / hkv;
-  int64_t s0 = 0;
-  int L = a.total;
-  if (a.cu) {
-    s0 = a.cu[blockIdx.y];
-    L = a.cu[blockIdx.y + 1] - (int)s0;
-  }
-  const int ntiles = (L + C::BM - 1) / C::BM;
-  if (pair >= (ntiles + 1) / 2) return;
-
-  const uint8_t* kbase = a.k + ((s0 * hkv + kvh) * DH) * 2;
-  const uint8_t* vbase = a.v + ((s0 * hkv + kvh) * DH) * 2;
-  const int64_t kv_stride = (int64_t)hkv * DH * 2;  // bytes between consecutive keys
-  uint8_t* gbase_a = lds_a + grp * C::STAGE;
-  uint8_t* gbase_b = lds_b + grp * C::STAGE;
-
-  // Gate bias and position of one key per thread (threads < 64 of a group),
-  // staged in registers; K and V go straight from global memory to LDS.
-  float breg = 0.0f;
-  int preg = 0;
-  // Gate bias in units of the raw score, times the head's gain.
-  const float inv_c = (a.head_gain ? a.head_gain[head] : 1.0f) / a.scale_log2;
-  // Direct load i of this thread fills LDS chunk P = i*256 + gtid of the tile:
-  // row P / CPR, stored position P % CPR, holding logical chunk pos ^ swz(row).
-  uint32_t dma_k[C::DMA], dma_v[C::DMA];
-  int dma_row[C::DMA];
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    const int P = i * 256 + gtid;
-    const int r = P / C::CPR, pos = P % C::CPR;
-    dma_row[i] = r;
-    dma_k[i] = (uint32_t)((pos ^ C::swz_k(r)) * 16);
-    dma_v[i] = (uint32_t)((pos ^ C::swz_v(r)) * 16);
-  }
-  const int wave_in_group = w4;
-  auto issue_tile = [&](int kt, uint8_t* sb) __attribute__((always_inline)) {
-    const bool full = (kt + 1) * C::BN <= L;
-#pragma unroll
-    for (int i = 0; i < C::DMA; ++i) {
-      const int j = full ? kt * C::BN + dma_row[i] : min(kt * C::BN + dma_row[i], L - 1);
-      const uint8_t* krow = kbase + (uint32_t)j * (uint32_t)kv_stride;
-      const uint8_t* vrow = vbase + (uint32_t)j * (uint32_t)kv_stride;
-      uint8_t* dst = sb + (i * 256 + wave_in_group * 64) * 16;  // wave-uniform; lane l lands at +16 l
-      __builtin_amdgcn_global_load_lds((const void*)(krow + dma_k[i]),
-                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vrow + dma_v[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + C::K_BYTES), 16, 0, 0);
-    }
-    if (gtid < C::BN) {
-      const int j = kt * C::BN + gtid;
-      if (j < L) {
-        breg = a.g ? a.g[s0 + j] : 1.0f;
-        preg = a.pos[s0 + j];
-      } else {
-        breg = -INFINITY;
-        preg = 0x7fffffff;
-      }
-    }
-  };
-  // Completes a tile issued by issue_tile: bias and positions into LDS after
-  // every outstanding global load (the direct K/V loads included) has landed.
-  auto finish_tile = [&](uint8_t* sb) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0)
-    if (gtid < C::BN) {
-      // Gate bias in units of the raw score: log2(g) / (scale*log2 e), so that
-      // it can seed the S^T accumulator and enter the logit inside the MFMA.
-      reinterpret_cast<float*>(sb + C::K_BYTES + C::V_BYTES)[gtid] =
-          (breg == -INFINITY) ? -INFINITY : log2f(fmaxf(breg, kFltMin)) * inv_c;
-      reinterpret_cast<int*>(sb + C::K_BYTES + C::V_BYTES + C::BN * 4)[gtid] = preg;
-    }
-  };
-  // K fragment offsets (per k-step) and V^T transposing-read offsets (per
-  // 32-row block of d), including the swizzles.
-  uint32_t koff[DH / 16];
-#pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks) koff[ks] = r32 * C::ROW + (((2 * ks + half) ^ C::swz_k(r32)) * 16);
-  const int G = lane >> 4, ia = (lane >> 2) & 3, ib = lane & 3;
-  uint32_t voff[C::MD];
-#pragma unroll
-  for (int md = 0; md < C::MD; ++md) {
-    const int vrow = 4 * (G >> 1) + ia;             // + 16 kb + 8 rr (multiples of 8 keep the swizzle)
-    const int chunk = 4 * md + 2 * (G & 1) + (ib >> 1);
-    voff[md] = C::K_BYTES + vrow * C::ROW + ((chunk ^ C::swz_v(vrow)) * 16) + (ib & 1) * 8;
-  }
-
-  for (int which = 0; which < 2; ++which) {
-    const int mt = which == 0 ? ntiles - 1 - pair : pair;
-    if (which == 1 && mt == ntiles - 1 - pair) break;  // middle tile of an odd count
-
-    const int row0 = mt * C::BM;
-    const int qi = row0 + w4 * 32 + r32;
-    const int qrow = qi < L ? qi : L - 1;
-    const uint8_t* qp = a.q + (((s0 + qrow) * hq + head) * DH) * 2;
-    bf16x8 qf[DH / 16];
-#pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (ks * 16 + half * 8) * 2);
-    const int pos_i = a.pos[s0 + qrow];
-    // Q fragments must have landed before the loop: otherwise the wait-count
-    // bookkeeping at the loop header merges them with the in-flight prefetch
-    // and every QK^T MFMA waits on the next tile's global loads.
-    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0): gfx9 encoding, lgkm/exp counts untouched
-
-    const int kend = min(L, row0 + C::BM);
-    const int n_kt = (kend + C::BN - 1) / C::BN;
-    const int niter = (n_kt + 1) / 2;
-
-    float m = -INFINITY;
-    float lsum = 0.0f;
-    f32x16 oacc[C::MD];
-#pragma unroll
-    for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
-
-    if (grp < n_kt) {
-      issue_tile(grp, gbase_a);
-      finish_tile(gbase_a);
-    }
-    __syncthreads();
-
-    auto step = [&](int it, uint8_t* cur, uint8_t* nb) __attribute__((always_inline)) {
-      const int kt = 2 * it + grp;
-      const int nxt = kt + 2;
-      if (nxt < n_kt) issue_tile(nxt, nb);
-      if (kt < n_kt) {
-        const uint8_t* sb = cur;
-        // ---- S^T = bias + K Q^T for 64 keys x this wave's 32 queries ----
-        const float* bias = reinterpret_cast<const float*>(sb + C::K_BYTES + C::V_BYTES);
-        f32x16 sacc[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const f32x4 bj = *reinterpret_cast<const f32x4*>(bias + mb * 32 + 8 * rq + 4 * half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sacc[mb][4 * rq + e] = bj[e];
-          }
-#pragma unroll
-        for (int ks = 0; ks < DH / 16; ++ks) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + mb * 32 * C::ROW + koff[ks]);
-            sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
-          }
-        }
-        // ---- online softmax (base 2); logits t = c * S^T ----
-        const int* kpos = reinterpret_cast<const int*>(sb + C::K_BYTES + C::V_BYTES + C::BN * 4);
-        // Causal test only on tiles reaching past this wave's first query.
-        if (kt * C::BN + C::BN - 1 > row0 + w4 * 32) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const u32x4 pj = *reinterpret_cast<const u32x4*>(kpos + mb * 32 + 8 * rq + 4 * half);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                sacc[mb][4 * rq + e] = ((int)pj[e] > pos_i) ? -INFINITY : sacc[mb][4 * rq + e];
-            }
-        }
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mb][r]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float m_new = fmaxf(m, mloc * a.scale_log2);
-        // The reference maximum m is only moved when some lane's logits exceed
-        // it by more than 8 (log2 units): until then p = 2^(t - m) <= 256, which
-        // fp32 accumulators and bf16 weights hold exactly as well as p <= 1,
-        // and numerator and denominator share the same shift.  This skips the
-        // O rescale on most tiles.
-        if (__any(m_new > m + 8.0f)) {
-          const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-          lsum *= alpha;
-#pragma unroll
-          for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-          m = m_new;
-        }
-        const float msub = (m == -INFINITY) ? 0.0f : m;
-        float psum = 0.0f;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + e], a.scale_log2, -msub));
-            psum += p;
-            pf[kb][e] = (__bf16)p;
-          }
-        lsum += psum;
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-          for (int md = 0; md < C::MD; ++md) {
-            const uint8_t* vp = sb + voff[md] + (16 * kb) * C::ROW;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * C::ROW));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb], oacc[md], 0, 0, 0);
-          }
-        }
-      }
-      if (nxt < n_kt) finish_tile(nb);
-      __syncthreads();
-    };
-    for (int it = 0; it < niter; it += 2) {
-      step(it, gbase_a, gbase_b);
-      if (it + 1 < niter) step(it + 1, gbase_b, gbase_a);
-    }
-
-    // ---- merge the two groups' partial results, normalise, store ----
-    float* scr = reinterpret_cast<float*>(lds_a);
-    float* scr_m = reinterpret_cast<float*>(lds_b);
-    float* scr_l = scr_m + 4 * 64;
-    if (grp == 1) {
-#pragma unroll
-      for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(w4 * (DH / 2) + md * 16 + r) * 64 + lane] = oacc[md][r];
-      scr_m[w4 * 64 + lane] = m;
-      scr_l[w4 * 64 + lane] = lsum;
-    }
-    __syncthreads();
-    if (grp == 0) {
-      const float m1 = scr_m[w4 * 64 + lane];
-      const float l1 = scr_l[w4 * 64 + lane];
-      const float mt_ = fmaxf(m, m1);
-      const float a0 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mt_);
-      const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - mt_);
-      float l = lsum * a0 + l1 * a1;
-      l += __shfl_xor(l, 32, kWave);
-      const float inv = 1.0f / l;
-      if (qi < L) {
-        uint8_t* op = a.o + (((s0 + qi) * hq + head) * DH) * 2;
-#pragma unroll
-        for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float ov[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rq + e;
-              ov[e] = (oacc[md][r] * a0 + scr[(w4 * (DH / 2) + md * 16 + r) * 64 + lane] * a1) * inv;
-            }
-            const u32x2 packed = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-            *reinterpret_cast<u32x2*>(op + (md * 32 + 8 * rq + 4 * half) * 2) = packed;
-          }
-        if (a.lse && half == 0) a.lse[(int64_t)head * a.total + s0 + qi] = (mt_ + log2f(l)) * kLn2;
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // ---------------------------------------------------------------------------
-// bf16 ping-pong kernel, used when the bias of every kept key fits in LDS.
+// bf16 ping-pong kernel.
 //
-// Same workgroup shape and key split as attn_bf16_kernel (8 waves, group g
-// takes the key tiles kt = 2t + g), but the two waves on each SIMD (one per
-// group) never run the same kind of work at the same time.  Work is cut into
+// 8 waves; group g takes the key tiles kt = 2t + g, and the two waves on each
+// SIMD (one per group) never run the same kind of work at the same time.  Work is cut into
 // slots separated by workgroup barriers.  Each group alternates
 //   MFMA slot t:  O^T += V^T P^T for its tile t-1, then S^T = K Q^T for tile t
 //   VALU slot t:  online softmax of tile t (P^T for the next MFMA slot)
@@ -386,8 +94,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 // SIMD feeds the matrix core while the other runs the exp/max/sum VALU work.
 // K and V have their own double buffers: K(t+2) and V(t+1) are copied in at
 // the start of VALU slot t, three slots before they are read.  The gate bias
-// of every key is computed once per workgroup into LDS, so the pipelined
-// region holds no register loads from global memory at all.  Keys are
+// comes from LDS (a table built once per tile pair, or a ring the copies
+// feed), so the pipelined region holds no register loads from global memory.  Keys are
 // visible when their kept index is at most the query's: with strictly
 // increasing positions (the contract of the entry point) that is the same
 // test as comparing positions.
@@ -396,7 +104,13 @@ struct PPCfg {
   static constexpr int MAXK = DH == 128 ? 8192 : 16384;  // keys whose bias fits in LDS
 };
 
-template <int DH>
+// STREAM = false: the bias of every key the workgroup can see sits in one LDS
+// table, built once per tile pair (prompts up to MAXK keys, or no gate).
+// STREAM = true: wave 0 of each group copies the raw gate values of the
+// group's key tile t+3 together with the other copies of batch t and, inside
+// MFMA slot t, turns those of tile t+1 into its bias in a two-slot LDS ring:
+// any prompt length, at a few percent more per tile.
+template <int DH, bool STREAM>
 __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   using C = AttnCfg<DH>;
   constexpr int KB = C::K_BYTES;  // one group's K (or V) tile
@@ -406,7 +120,9 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t k_s1[2 * KB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_s0[2 * KB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_s1[2 * KB];
-  __shared__ __attribute__((aligned(16))) float bias_all[MAXK];
+  __shared__ __attribute__((aligned(16))) float bias_all[STREAM ? 1 : MAXK];
+  __shared__ __attribute__((aligned(16))) float graw[2][STREAM ? 4 : 1][BN];    // per group, 4 tile slots
+  __shared__ __attribute__((aligned(16))) float bias_s[2][STREAM ? 2 : 1][BN];  // per group, 2 tile slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -491,6 +207,23 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     }
   };
 
+  // STREAM: raw gate values of this group's tile t (keys (2t + grp) * BN..)
+  // into slot t % 4 by wave 0 of the group, lanes past the prompt re-reading
+  // its last key; the bias of tile t from them, by the same wave (so its own
+  // copy wait covers the data), into slot t % 2.
+  const float inv_c = gain / c;  // gate bias times the head's gain
+  const bool g_wave = STREAM && w4 == 0;
+  auto issue_g = [&](int t) __attribute__((always_inline)) {
+    if (g_wave) dma4(a.g + s0 + min((2 * t + grp) * BN + lane, L - 1),
+                     lds_addr(reinterpret_cast<uint8_t*>(&graw[grp][t & 3][0])));
+  };
+  // The input is clamped to a normal number, where the hardware log2 is what
+  // log2f computes.
+  auto bias_of = [&](int t, float gj) __attribute__((always_inline)) {
+    return (2 * t + grp) * BN + lane >= L ? -INFINITY : __builtin_amdgcn_logf(fmaxf(gj, kFltMin)) * inv_c;
+  };
+  auto g_count = [&](int t) __attribute__((always_inline)) { return (g_wave && t < niter) ? 1 : 0; };
+
   // ---- prologue: Q fragments and gate values (register loads) first, then
   // the first copies, so the register loads can be waited for while the
   // copies keep landing.
@@ -503,7 +236,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   // query tile can see (rounded up to whole key tiles); keys past the prompt
   // get -inf.
   const int nb = n_kt * BN;
-  constexpr int GPT = (MAXK + 511) / 512;
+  constexpr int GPT = STREAM ? 1 : (MAXK + 511) / 512;
   float gv[GPT];
   // Unconditional loads at a clamped index: a predicated load would let the
   // compiler sink each log2 into its own branch and wait for every load in turn.
@@ -511,27 +244,37 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   // values unused): a NULL test inside the loop would split the loads into
   // branches that each wait for their own load.
   const float* gsrc = has_gate ? a.g + s0 : reinterpret_cast<const float*>(a.pos + s0);
-  if (pass == 0) {
+  if (!STREAM && pass == 0) {
 #pragma unroll
     for (int i = 0; i < GPT; ++i) gv[i] = gsrc[min(tid + 512 * i, L - 1)];
   }
-  // Copies per wave in batch b (K of tile b+2, V of tile b+1); here go batch
-  // -2 (K(0)) and batch -1 (K(1), V(0)).
+  // Copies per wave in batch b: K of tile b+2, V of tile b+1 (and, STREAM,
+  // the gate values of tile b+3); here go the gate values of tile 0, batch
+  // -2 (K(0), g(1)) and batch -1 (K(1), V(0), g(2)).
+  if (0 < niter) issue_g(0);
   if (0 < niter) issue(kbase, off_k, grp, k_addr[0]);
+  if (1 < niter) issue_g(1);
   if (1 < niter) issue(kbase, off_k, 2 + grp, k_addr[1]);
   if (0 < niter) issue(vbase, off_v, grp, v_addr[0]);
+  if (2 < niter) issue_g(2);
   {
-    const int nc = (0 < niter ? 2 * C::DMA : 0) + (1 < niter ? C::DMA : 0);
-    if (nc == 3 * C::DMA)
-      wait_vm<3 * C::DMA>();  // Q and g have landed; the copies may not have
+    // Q, g and the gate values of tile 0 have landed once at most the two
+    // batches are outstanding; the copies may not have.
+    const int nc = (0 < niter ? 2 * C::DMA : 0) + (1 < niter ? C::DMA : 0) + g_count(1) + g_count(2);
+    if (nc == 3 * C::DMA + 2)
+      wait_vm<3 * C::DMA + 2>();
+    else if (nc == 3 * C::DMA + 1)
+      wait_vm<3 * C::DMA + 1>();
+    else if (nc == 3 * C::DMA)
+      wait_vm<3 * C::DMA>();
     else if (nc == 2 * C::DMA)
       wait_vm<2 * C::DMA>();
     else
       wait_vm<0>();
   }
-  if (pass == 0 && !has_gate && tid < BN) bias_all[tid] = 0.0f;
-  if (pass == 0 && a.g) {
-    const float inv_c = gain / c;  // gate bias times the head's gain
+  if (g_wave && 0 < niter) bias_s[grp][0][lane] = bias_of(0, graw[grp][0][lane]);
+  if (!STREAM && pass == 0 && !has_gate && tid < BN) bias_all[tid] = 0.0f;
+  if (!STREAM && pass == 0 && a.g) {
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
       const int j = tid + 512 * i;
@@ -554,7 +297,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
 
   {
     auto batch_count = [&](int b) __attribute__((always_inline)) {
-      return ((b + 2 < niter) ? C::DMA : 0) + ((b + 1 >= 0 && b + 1 < niter) ? C::DMA : 0);
+      return ((b + 2 < niter) ? C::DMA : 0) + ((b + 1 >= 0 && b + 1 < niter) ? C::DMA : 0) + g_count(b + 3);
     };
 
     float m = -INFINITY;
@@ -567,13 +310,19 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     f32x16 sacc[2];
     bf16x8 pf[4];
 
-    // K(t) and V(t-1) came with batch t-2; batch t-1 may still be landing.
+    // K(t), V(t-1) (and g(t+1)) came with batch t-2; batch t-1 may still be landing.
     auto wait_for_tile = [&](int t) __attribute__((always_inline)) {
       const int nf = batch_count(t - 1);
-      if (nf == 2 * C::DMA)
+      if (nf == 2 * C::DMA + 1)
+        wait_vm<2 * C::DMA + 1>();
+      else if (nf == 2 * C::DMA)
         wait_vm<2 * C::DMA>();
+      else if (nf == C::DMA + 1)
+        wait_vm<C::DMA + 1>();
       else if (nf == C::DMA)
         wait_vm<C::DMA>();
+      else if (nf == 1)
+        wait_vm<1>();
       else
         wait_vm<0>();
     };
@@ -586,6 +335,12 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       // Higher issue priority while this wave feeds the matrix core; the
       // other wave on the SIMD (in its VALU slot) fills the gaps.
       __builtin_amdgcn_s_setprio(2);
+      // STREAM: the bias of tile t+1 from its gate values (batch t-2), read
+      // now and written after the PV products, so the LDS latency and the
+      // log2 hide behind the matrix work.
+      const bool next_bias = g_wave && t + 1 < niter;
+      float g_next = 0.0f;
+      if (next_bias) g_next = graw[grp][(t + 1) & 3][lane];
       if (t >= 1 && t - 1 < niter) {
         const uint8_t* vs = ((t - 1) & 1 ? v_s1 : v_s0) + grp * KB;
         bf16x8 vf[2][C::MD];
@@ -612,12 +367,16 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if (next_bias) {
+        bias_s[grp][(t + 1) & 1][lane] = bias_of(t + 1, g_next);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): written before the next barrier
+      }
       if (t < niter) {
         const int kt = 2 * t + grp;
         const uint8_t* ksb = (t & 1 ? k_s1 : k_s0) + grp * KB;
         // Without a gate every tile reads the 64 zeros at the start of the table
         // (keys past the prompt are then removed by the causal test).
-        const float* bias = bias_all + (has_gate ? kt * BN : 0);
+        const float* bias = STREAM ? &bias_s[grp][t & 1][0] : bias_all + (has_gate ? kt * BN : 0);
         bf16x8 kf[2][2][2];  // [buffer][k-step within the pair][32-key half]
         auto load_k = [&](int kp, bf16x8 (*dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -655,6 +414,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       if (t < 0) return;
       if (t + 2 < niter) issue(kbase, off_k, 2 * (t + 2) + grp, k_addr[t & 1]);
       if (t + 1 < niter) issue(vbase, off_v, 2 * (t + 1) + grp, v_addr[(t + 1) & 1]);
+      if (t + 3 < niter) issue_g(t + 3);
       if (t >= niter) return;
       const int kt = 2 * t + grp;
       if (kt * BN + BN - 1 > row0 + w4 * 32) {  // tile reaches past this wave's first query
@@ -897,14 +657,14 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   const int64_t keys = (max_seqlen + 63) / 64 * 64;
   if (dh == 128) {
     if (!g || keys <= PPCfg<128>::MAXK)
-      hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<128, false>), grid, dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<128, true>), grid, dim3(512), 0, stream, a);
   } else {
     if (!g || keys <= PPCfg<64>::MAXK)
-      hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<64, false>), grid, dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<64, true>), grid, dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -46,6 +46,11 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
 }
 
+// 4-byte copy: lane l's dword lands at lds_addr + 4 l.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
+}
+
 // Same copy from a wave-uniform 64-bit base (scalar registers) plus a 32-bit
 // per-lane byte offset: one vector register per copy instead of two.
 __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {

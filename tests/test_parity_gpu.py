@@ -357,8 +357,8 @@ def test_attn_bf16_full_size_sampled_rows(gpu_lib, name, gkind):
 
 @pytest.mark.parametrize("n,dh", [(8300, 128), (16500, 64)])
 def test_attn_bf16_past_the_lds_bias_table(gpu_lib, n, dh):
-    """Kept counts above the ping-pong kernel's LDS bias table (8192 keys at
-    head dim 128, 16384 at 64) take the streaming-bias kernel."""
+    """Kept counts above the LDS bias table (8192 keys at head dim 128, 16384 at
+    64) take the kernel's streamed-bias form (gate values copied tile by tile)."""
     _say("attn long prompt", n, dh)
     q, k, v, g, pos = _attn_inputs(n, 2, 1, dh, torch.bfloat16, 31, "wide")
     o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
@@ -392,7 +392,7 @@ def test_attn_head_gain(gpu_lib, dtype, n, hq, hkv, dh):
     assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= tol_l
 
 
-def test_attn_head_gain_on_the_streaming_bias_kernel(gpu_lib):
+def test_attn_head_gain_on_the_streamed_bias_form(gpu_lib):
     n = 8300  # past the LDS bias table at head dim 128
     q, k, v, g, pos = _attn_inputs(n, 2, 1, 128, torch.bfloat16, 42, "wide")
     gain = torch.tensor([0.5, 1.75], dtype=torch.float32)
