@@ -437,6 +437,33 @@ def test_attn_varlen_with_head_gain(gpu_lib):
     assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= 1e-3
 
 
+def test_attn_varlen_streamed_bias_with_head_gain(gpu_lib):
+    """A packed batch whose longest prompt passes the LDS bias table (9000 keys at
+    head dim 128) runs every prompt in the streamed-bias form: ragged lengths, an
+    empty prompt, per-head gains; the long prompt on sampled rows."""
+    lens = [9000, 300, 0, 77]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    _say("attn varlen streamed bias", lens)
+    q, k, v, g, _ = _attn_inputs(total, 4, 2, 128, torch.bfloat16, 46, "wide")
+    pos = torch.from_numpy(np.concatenate([np.arange(m) * 2 for m in lens]).astype(np.int32))
+    gain = _gains(4, 46)
+    o, lse = gpu_lib.tg_gated_attn_varlen(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV),
+                                          torch.from_numpy(cu).to(DEV), max(lens), want_lse=True,
+                                          head_gain=gain.to(DEV))
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    for b, m in enumerate(lens):
+        if m == 0:
+            continue
+        s0 = int(cu[b])
+        sl = slice(s0, s0 + m)
+        rows = _sample_rows(m, 7 + b, count=40) if m > 2000 else np.arange(m)
+        wo, wl = ref_attn(q[sl], k[sl], v[sl], g[sl], pos[sl].numpy(), rows=rows, head_gain=gain.numpy())
+        assert np.max(np.abs(o[s0 + rows] - wo)) <= 2e-2, f"prompt {b}"
+        assert np.max(np.abs(lse[:, s0 + rows] - wl)) <= 1e-3, f"prompt {b}"
+
+
 def test_attn_varlen_ragged(gpu_lib):
     lens = [256, 1, 100, 256, 129, 0, 256]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
