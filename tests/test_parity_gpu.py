@@ -528,20 +528,45 @@ def test_end_to_end_qwen_32k(gpu_lib):
 
 
 def test_repeat_runs_are_bitwise_identical(gpu_lib):
+    """Ten runs of every stage on the same inputs give the same bytes: the gate,
+    both selects (the multi-workgroup one builds its histograms with device
+    atomics, whose order must not matter), gather, RoPE + KV, attention, decode
+    and a dense product."""
     tg = gpu_lib
-    g = W.random_scores(32768, 2).to(DEV)
-    q, k, v, gk, pos = _attn_inputs(1000, 16, 8, 128, torch.bfloat16, 4)
-    q, k, v, gk, pos = (t.to(DEV) for t in (q, k, v, gk, pos))
+    _say("repeat runs")
+    n, d, hidden, k, q_len = 32768, 2048, 256, 4096, 64
+    h = W.hidden_states(n, d, torch.bfloat16, 12, planted_frac=0.05).to(DEV)
+    w1, b1, w2, b2 = W.gate_weights(d, hidden, torch.bfloat16, 12)
+    w1, b1, w2 = w1.to(DEV), b1.to(DEV), w2.to(DEV)
+    g = W.random_scores(n, 2).to(DEV)
+    ws = torch.empty(tg.tg_select_topk_workspace_size(n), dtype=torch.uint8, device=DEV)
+    q, kk, vv, gk, pos = _attn_inputs(1000, 16, 8, 128, torch.bfloat16, 4)
+    q, kk, vv, gk, pos = (t.to(DEV) for t in (q, kk, vv, gk, pos))
+    table = tg.tg_rope_table(4096, 128, 1e6, DEV)
+    cu = torch.tensor([0, 600, 1000], dtype=torch.int32, device=DEV)
+    qn = W.qkv(2, 16, 8, 128, 1.0 / 128, torch.bfloat16, 13)[0].to(DEV)
+    x = W.hidden_states(300, 2048, torch.bfloat16, 14).to(DEV)
+    wl = W.linear_weight(512, 2048, torch.bfloat16, 14).to(DEV)
     first = None
-    for _ in range(5):
-        idx = tg.tg_select_topk(g, 4096, 64)
-        o = tg.tg_gated_attn(q, k, v, gk, pos)
+    for _ in range(10):
+        gg = tg.tg_gate_score(h, w1, b1, w2, b2)
+        idx = tg.tg_select_topk(g, k, q_len)
+        idx_ws = tg.tg_select_topk_ws(g, k, q_len, workspace=ws)
+        hk, gk2, pk = tg.tg_gather(h, gg, idx)
+        qr = q.clone()
+        _, kc, vc = tg.tg_rope_kv(qr, kk, vv, pos, table)
+        o = tg.tg_gated_attn(q, kk, vv, gk, pos)
+        od = tg.tg_decode_attn(qn, kk, vv, gk, cu, 600)
+        y = tg.tg_linear(x, wl)
         torch.cuda.synchronize()
-        cur = (idx.cpu(), o.cpu())
+        cur = [t.cpu().view(torch.int16) if t.dtype == torch.bfloat16 else t.cpu()
+               for t in (gg, idx, idx_ws, hk, gk2, pk, qr, kc, vc, o, od, y)]
         if first is None:
             first = cur
+            assert torch.equal(idx, idx_ws)
         else:
-            assert torch.equal(cur[0], first[0]) and torch.equal(cur[1].view(torch.int16), first[1].view(torch.int16))
+            for a, b in zip(cur, first):
+                assert torch.equal(a, b)
 
 
 # ----------------------------------------------------------------------------- decode
