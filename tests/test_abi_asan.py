@@ -1,10 +1,10 @@
 """The C ABI's host code under AddressSanitizer (no GPU needed).
 
 Builds every translation unit of the library with AddressSanitizer on its host
-code only (the device code is compiled as usual), links tests/abi_asan_driver.cpp
-against it and runs the driver: each of its calls is refused by host-side
-validation before any HIP call, so the run checks that argument validation and
-error reporting of every entry point stay inside their memory."""
+code only (the device code is compiled as usual), links the test program
+tests/abi_asan_driver.cpp against it and runs it: each of its calls is refused
+by host-side validation before any HIP call, so the run checks that argument
+validation and error reporting of every entry point stay inside their memory."""
 import concurrent.futures as cf
 import os
 import shutil
