@@ -370,11 +370,26 @@ def cpu_baseline(W, name):
         "kind": "oracle",
         "sample": (f"numpy fp64 oracle on the same seeded {name} inputs: gate on {rows_gate} of {sh.n} rows, "
                    f"full select/gather/RoPE, attention on 512 of {kk} query rows (all heads); each stage "
-                   f"scaled to the full prompt"),
+                   f"scaled to the full prompt"
+                   + (f"; RoPE + attention timed for one upper layer, x{sh.layers} extrapolated" if sh.layers > 1
+                      else "")),
         "stage_s": {"gate": t_gate, "select": t_sel, "gather": t_gat, "rope_kv": t_rope, "attn": t_attn},
         "host_cpus": os.cpu_count(),
+        "cpu_model": _cpu_model(),
         "next_rows": cpu_next_rows(W, sh),
     }
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_next_rows(W, sh, batch=32):
