@@ -200,6 +200,17 @@ def graph_steps(torch, path, steps, warmup):
     return {"ms_per_step": round(ms, 4), "tokens/s": round(path.sh.n / (ms * 1e-3), 1), "steps": steps}
 
 
+SPIN_CYCLES = 100_000  # GPU clock cycles of the spin kernel queued ahead of a timed call
+
+
+def queue_ahead(torch):
+    """Keep the stream busy for a few tens of microseconds (torch's spin
+    kernel) before a start event, so that the event is processed after the
+    host has queued the work it times: an event pair around work launched onto
+    an idle stream also measures the host's launch latency."""
+    torch.cuda._sleep(SPIN_CYCLES)
+
+
 def time_stages(path, reps):
     import torch
     sh = path.sh
@@ -207,6 +218,7 @@ def time_stages(path, reps):
     samples = {n: [] for n in names}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
     for _ in range(reps):
+        queue_ahead(torch)
         ev[0].record()
         path.gate()
         ev[1].record()
@@ -270,6 +282,7 @@ def upper_layer(tg, W, sh, dev, m, gated, reps=8):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
     times = {n: [] for n, _ in stages}
     for r in range(reps + 1):
+        queue_ahead(torch)
         ev[0].record()
         for i, (_, fn) in enumerate(stages):
             fn()
@@ -312,6 +325,7 @@ def decode_step(tg, W, sh, dev, batch=32, reps=20):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ts = []
     for r in range(reps + 2):
+        queue_ahead(torch)
         ev[0].record()
         tg.tg_decode_attn(q, kc, vc, g, cu, max(lens), o=o, lse=lse, workspace=ws)
         ev[1].record()
