@@ -27,8 +27,8 @@
  *    without synchronising.  Calls are thread-safe; calls on different streams
  *    may run concurrently if their output buffers do not overlap.
  *  - Arguments are validated on the host before any HIP call.  A failed check
- *    returns TG_ERR_INVALID_ARG or TG_ERR_UNSUPPORTED, enqueues nothing and sets
- *    the message returned by tg_last_error().  A launch failure reported by HIP
+ *    returns TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED or TG_ERR_WORKSPACE,
+ *    enqueues nothing and sets the message returned by tg_last_error().  A launch failure reported by HIP
  *    returns TG_ERR_HIP.  Faults inside a kernel surface at the caller's next
  *    synchronisation.
  *  - n == 0 (nothing to do) returns TG_OK and enqueues nothing.
@@ -65,7 +65,8 @@ typedef enum tg_status {
   TG_OK = 0,
   TG_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, inconsistent sizes */
   TG_ERR_UNSUPPORTED = 2, /* valid request that this build has no kernel for */
-  TG_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+  TG_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+  TG_ERR_WORKSPACE = 4    /* caller workspace smaller than its size function asks for */
 } tg_status;
 
 typedef enum tg_dtype {
@@ -143,8 +144,8 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
  * share a workspace must be ordered on one stream.  Budgets that keep the
  * whole document or none of it, and documents above 2^24 tokens, run the
  * one-workgroup kernel of tg_select_topk instead.
- * Errors: as tg_select_topk; a NULL, misaligned or too small workspace ->
- * INVALID_ARG. */
+ * Errors: as tg_select_topk; a NULL or misaligned workspace -> INVALID_ARG;
+ * a workspace smaller than tg_select_topk_workspace_size(n) -> WORKSPACE. */
 TG_API int64_t tg_select_topk_workspace_size(int64_t n); /* -1 for n outside [0, 2^31) */
 TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t q_len,
                                    int32_t* idx, void* workspace, int64_t workspace_bytes,
@@ -315,9 +316,10 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
  *               the key blocks; contents need not be initialised and are
  *               left undefined.  Calls that share a workspace must not
  *               overlap.  The library allocates nothing.
- * Errors: TG_ERR_INVALID_ARG for NULL pointers, misalignment, a too-small
- * workspace or out-of-range sizes; TG_ERR_UNSUPPORTED for other head ratios
- * or dh; TG_ERR_HIP for a failed launch.  batch = 0 is a no-op.
+ * Errors: TG_ERR_INVALID_ARG for NULL pointers, misalignment or out-of-range
+ * sizes; TG_ERR_WORKSPACE for a workspace smaller than the size function
+ * returns; TG_ERR_UNSUPPORTED for other head ratios or dh; TG_ERR_HIP for a
+ * failed launch.  batch = 0 is a no-op.
  * ------------------------------------------------------------------------- */
 TG_API int64_t tg_decode_attn_workspace_size(int32_t batch, int64_t max_seqlen, int32_t hq,
                                              int32_t hkv, int32_t dh);

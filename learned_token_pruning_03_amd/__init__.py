@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     TG_ERR_HIP,
     TG_ERR_INVALID_ARG,
     TG_ERR_UNSUPPORTED,
+    TG_ERR_WORKSPACE,
     TG_FP32,
     TG_OK,
     TokenGateError,

@@ -18,7 +18,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtokengate.so")
 
-TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_HIP = 0, 1, 2, 3
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_HIP, TG_ERR_WORKSPACE = 0, 1, 2, 3, 4
 TG_FP32, TG_BF16 = 0, 1
 
 _c_vp = ctypes.c_void_p

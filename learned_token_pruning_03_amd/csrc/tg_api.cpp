@@ -56,6 +56,7 @@ TG_API const char* tg_status_string(int status) {
     case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG";
     case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
     case TG_ERR_HIP: return "TG_ERR_HIP";
+    case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE";
     default: return "TG_UNKNOWN_STATUS";
   }
 }
@@ -126,7 +127,7 @@ TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t
   if (!aligned16(workspace)) return fail(TG_ERR_INVALID_ARG, "select_ws: workspace must be 16-byte aligned");
   const int64_t need = tg::select_mw_workspace_bytes(n);
   if (workspace_bytes < need)
-    return fail(TG_ERR_INVALID_ARG, "select_ws: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+    return fail(TG_ERR_WORKSPACE, "select_ws: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
                 (long long)need);
   return from_hip(tg::launch_select_mw(g, n, k, q_len, idx, workspace, stream), "select_ws");
 }
@@ -346,7 +347,7 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
     return fail(TG_ERR_INVALID_ARG, "decode: q, k_cache, v_cache and workspace must be 16-byte aligned");
   const int64_t need = decode_ws_bytes(batch, max_seqlen, hq, hkv, dh);
   if (workspace_bytes < need)
-    return fail(TG_ERR_INVALID_ARG, "decode: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+    return fail(TG_ERR_WORKSPACE, "decode: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
                 (long long)need);
   return from_hip(tg::launch_decode(elem_size(dtype), cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q,
                                     k_cache, v_cache, g, head_gain, o, lse, static_cast<float*>(workspace),

@@ -44,6 +44,7 @@ def test_status_strings_and_version(lib):
     assert lib.tg_abi_version() == 1
     assert tg.status_string(0) == "TG_OK"
     assert tg.status_string(1) == "TG_ERR_INVALID_ARG"
+    assert tg.status_string(4) == "TG_ERR_WORKSPACE"
     assert tg.status_string(99) == "TG_UNKNOWN_STATUS"
 
 
@@ -127,7 +128,7 @@ def test_decode_validation_without_a_gpu(lib):
     assert call(scale=0.0) == tg.TG_ERR_INVALID_ARG
     assert call(q=None) == tg.TG_ERR_INVALID_ARG
     assert call(cu=None) == tg.TG_ERR_INVALID_ARG
-    assert call(ws_bytes=ws - 4) == tg.TG_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 4) == tg.TG_ERR_WORKSPACE
     assert b"workspace" in lib.tg_last_error()
     assert call(max_seqlen=-1) == tg.TG_ERR_INVALID_ARG
     big = lib.tg_decode_attn_workspace_size(70000, 5000, 16, 8, 128)
@@ -222,7 +223,7 @@ def test_select_ws_validation_without_a_gpu(lib):
     assert ws >= (2048 + 2048 + 1024 + 16 * 2) * 4  # three histograms, two counts per 2048-key chunk
     assert lib.tg_select_topk_workspace_size(-1) == -1
     ok = tg.TG_ERR_INVALID_ARG
-    assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == ok  # too small
+    assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == tg.TG_ERR_WORKSPACE
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, None, ws, None) == ok  # NULL workspace
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE + 4, ws, None) == ok  # misaligned
     assert lib.tg_select_topk_ws(FAKE, 32768, 10, 11, FAKE, FAKE, ws, None) == ok  # q_len > budget
