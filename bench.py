@@ -344,11 +344,14 @@ def decode_step(tg, W, sh, dev, batch=32, reps=20):
             "tokens/s": round(batch / (us * 1e-6), 1)}
 
 
+ATTN_SAMPLE_ROWS = 4096  # query rows of the attention in the CPU baseline's sample (all, up to 4096 kept)
+
+
 def cpu_baseline(W, name):
-    """The oracle, untouched, on a bounded sample of the same workload, scaled
-    to the whole prompt: half of the gate rows, the full select and gather, the
-    full RoPE, and 512 random query rows of the attention (scaled by the exact
-    count of visible query-key pairs)."""
+    """The oracle, untouched, on a bounded sample of the same workload (about
+    ten seconds of host work), scaled to the whole prompt: the full gate,
+    select, gather and RoPE, and up to 4096 random query rows of the attention
+    (scaled by the exact count of visible query-key pairs)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -359,11 +362,11 @@ def cpu_baseline(W, name):
     h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac)
     w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
     q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed * 1000)
-    rows_gate = sh.n // 2
+    rows_gate = sh.n
     t0 = time.perf_counter()
     g, _ = O.ref_gate(h[:rows_gate], w1, b1, w2, b2)
     t_gate = (time.perf_counter() - t0) * sh.n / rows_gate
-    g_full = np.concatenate([g, g])[: sh.n].astype(np.float32)
+    g_full = g.astype(np.float32)
     t0 = time.perf_counter()
     idx = O.ref_select(g_full, sh.k, sh.q_len)
     t_sel = time.perf_counter() - t0
@@ -374,7 +377,8 @@ def cpu_baseline(W, name):
     O.ref_rope_kv(q, k, v, pos, sh.rope_base)
     t_rope = time.perf_counter() - t0
     kk = len(idx)
-    rows = np.sort(np.random.default_rng(seed).choice(kk, 512, replace=False))
+    n_rows = min(ATTN_SAMPLE_ROWS, kk)
+    rows = np.sort(np.random.default_rng(seed).choice(kk, n_rows, replace=False))
     t0 = time.perf_counter()
     O.ref_attn(q, k, v, gk, pos, rows=rows)
     t_attn = (time.perf_counter() - t0) * (kk * (kk + 1) / 2) / float(np.sum(rows + 1))
@@ -386,7 +390,7 @@ def cpu_baseline(W, name):
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"numpy fp64 oracle on the same seeded {name} inputs: gate on {rows_gate} of {sh.n} rows, "
-                   f"full select/gather/RoPE, attention on 512 of {kk} query rows (all heads); each stage "
+                   f"full select/gather/RoPE, attention on {n_rows} of {kk} query rows (all heads); each stage "
                    f"scaled to the full prompt"
                    + (f"; RoPE + attention timed for one upper layer, x{sh.layers} extrapolated" if sh.layers > 1
                       else "")),
@@ -411,21 +415,22 @@ def _cpu_model():
 
 def cpu_next_rows(W, sh, batch=32):
     """The oracle on the two later rows the bench also times on the GPU, each on
-    a bounded sample scaled to the full call: decode attention (4 of the 32
+    a bounded sample scaled to the full call: decode attention (16 of the 32
     sequences, caches of K keys) and one upper layer's dense work (QKV and O
-    projections, SwiGLU, down projection on 256 of the K kept rows)."""
+    projections, SwiGLU, down projection on 1024 of the K kept rows)."""
     import numpy as np
     import torch
 
     import oracle as O
-    q, _, _ = W.qkv(4, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 12)
-    _, kc, vc = W.qkv(4 * sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 13)
-    g = W.random_scores(4 * sh.k, 14)
-    cu = np.arange(5) * sh.k
+    nseq = 16
+    q, _, _ = W.qkv(nseq, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 12)
+    _, kc, vc = W.qkv(nseq * sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, 13)
+    g = W.random_scores(nseq * sh.k, 14)
+    cu = np.arange(nseq + 1) * sh.k
     t0 = time.perf_counter()
     O.ref_decode(q, kc, vc, g, cu)
-    t_dec = (time.perf_counter() - t0) * batch / 4
-    rows, d = 256, sh.d
+    t_dec = (time.perf_counter() - t0) * batch / nseq
+    rows, d = 1024, sh.d
     x = W.hidden_states(rows, d, sh.dtype, 21)
     w_qkv = W.linear_weight((sh.hq + 2 * sh.hkv) * sh.dh, d, sh.dtype, 22)
     w_o = W.linear_weight(d, sh.hq * sh.dh, sh.dtype, 23)
@@ -440,7 +445,7 @@ def cpu_next_rows(W, sh, batch=32):
     t_dense = (time.perf_counter() - t0) * sh.k / rows
     return {"decode_s": t_dec, "decode_tokens/s": batch / t_dec,
             "upper_dense_s": t_dense, "upper_dense_rows": sh.k,
-            "sample": f"decode: 4 of {batch} sequences with {sh.k}-key caches, scaled by {batch // 4}; "
+            "sample": f"decode: {nseq} of {batch} sequences with {sh.k}-key caches, scaled by {batch // nseq}; "
                       f"dense: {rows} of {sh.k} kept rows, scaled by {sh.k // rows}"}
 
 
