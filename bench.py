@@ -348,10 +348,11 @@ ATTN_SAMPLE_ROWS = 4096  # query rows of the attention in the CPU baseline's sam
 
 
 def cpu_baseline(W, name):
-    """The oracle, untouched, on a bounded sample of the same workload (about
-    ten seconds of host work), scaled to the whole prompt: the full gate,
-    select, gather and RoPE, and up to 4096 random query rows of the attention
-    (scaled by the exact count of visible query-key pairs)."""
+    """The oracle, untouched, on a bounded sample of the same workload (a few
+    to some tens of seconds of host work), scaled to the whole prompt: the full
+    gate, select, gather and RoPE, and up to 4096 random query rows of the
+    attention (scaled by the exact count of visible query-key pairs); one warm
+    pass, then per stage the median of three timed passes."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -363,25 +364,35 @@ def cpu_baseline(W, name):
     w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
     q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed * 1000)
     rows_gate = sh.n
-    t0 = time.perf_counter()
-    g, _ = O.ref_gate(h[:rows_gate], w1, b1, w2, b2)
-    t_gate = (time.perf_counter() - t0) * sh.n / rows_gate
-    g_full = g.astype(np.float32)
-    t0 = time.perf_counter()
-    idx = O.ref_select(g_full, sh.k, sh.q_len)
-    t_sel = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    hk, gk, pos = O.ref_gather(h.view(torch.int16).numpy(), g_full, idx)
-    t_gat = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.ref_rope_kv(q, k, v, pos, sh.rope_base)
-    t_rope = time.perf_counter() - t0
-    kk = len(idx)
-    n_rows = min(ATTN_SAMPLE_ROWS, kk)
-    rows = np.sort(np.random.default_rng(seed).choice(kk, n_rows, replace=False))
-    t0 = time.perf_counter()
-    O.ref_attn(q, k, v, gk, pos, rows=rows)
-    t_attn = (time.perf_counter() - t0) * (kk * (kk + 1) / 2) / float(np.sum(rows + 1))
+
+    def one_pass():
+        t0 = time.perf_counter()
+        g, _ = O.ref_gate(h[:rows_gate], w1, b1, w2, b2)
+        t_gate = (time.perf_counter() - t0) * sh.n / rows_gate
+        g_full = g.astype(np.float32)
+        t0 = time.perf_counter()
+        idx = O.ref_select(g_full, sh.k, sh.q_len)
+        t_sel = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        hk, gk, pos = O.ref_gather(h.view(torch.int16).numpy(), g_full, idx)
+        t_gat = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.ref_rope_kv(q, k, v, pos, sh.rope_base)
+        t_rope = time.perf_counter() - t0
+        kk = len(idx)
+        n_rows = min(ATTN_SAMPLE_ROWS, kk)
+        rows = np.sort(np.random.default_rng(seed).choice(kk, n_rows, replace=False))
+        t0 = time.perf_counter()
+        O.ref_attn(q, k, v, gk, pos, rows=rows)
+        t_attn = (time.perf_counter() - t0) * (kk * (kk + 1) / 2) / float(np.sum(rows + 1))
+        return kk, n_rows, {"gate": t_gate, "select": t_sel, "gather": t_gat, "rope_kv": t_rope, "attn": t_attn}
+
+    # One warm pass, then the median of three timed passes, stage by stage.
+    one_pass()
+    passes = [one_pass() for _ in range(3)]
+    kk, n_rows = passes[0][0], passes[0][1]
+    stage_s = {st: statistics.median(p[2][st] for p in passes) for st in passes[0][2]}
+    t_gate, t_sel, t_gat, t_rope, t_attn = (stage_s[st] for st in ("gate", "select", "gather", "rope_kv", "attn"))
     total = t_gate + t_sel + t_gat + sh.layers * (t_rope + t_attn)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
@@ -391,10 +402,10 @@ def cpu_baseline(W, name):
         "kind": "oracle",
         "sample": (f"numpy fp64 oracle on the same seeded {name} inputs: gate on {rows_gate} of {sh.n} rows, "
                    f"full select/gather/RoPE, attention on {n_rows} of {kk} query rows (all heads); each stage "
-                   f"scaled to the full prompt"
+                   f"scaled to the full prompt; median of 3 timed passes after a warm one"
                    + (f"; RoPE + attention timed for one upper layer, x{sh.layers} extrapolated" if sh.layers > 1
                       else "")),
-        "stage_s": {"gate": t_gate, "select": t_sel, "gather": t_gat, "rope_kv": t_rope, "attn": t_attn},
+        "stage_s": stage_s,
         "host_cpus": os.cpu_count(),
         "cpu_model": _cpu_model(),
         "next_rows": cpu_next_rows(W, sh),
