@@ -40,3 +40,6 @@ def test_bench_prints_one_json_line_with_the_roofline(gpu_lib):
     assert out["cpu_baseline"] is None  # switched off for this run
     for stage in ("gate", "select", "gather", "rope_kv", "attn"):
         assert out["stages"][stage]["median_us"] > 0
+    for stage in ("gate", "gather"):  # also timed back to back; the HBM fractions use that figure
+        assert out["stages"][stage]["us_back_to_back"] > 0
+    assert 0 < out["gather_pct_hbm_peak"] < 100 and 0 < out["gate_pct_hbm_peak"] < 100
