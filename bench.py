@@ -245,15 +245,17 @@ def time_stages(path, reps):
 
 
 def back_to_back(path, reps=30):
-    """Per-launch time of the gate and the gather when each runs `reps` times
-    in a row between one event pair (h rotating over its three copies, so no
-    launch finds its input in the last-level cache), so that the event pair's
-    own dispatch overhead, a few microseconds against a gather of about 8, is
-    spread over the launches; the gaps between the kernels stay in the
-    figure."""
+    """Per-launch time of the gate, the gather and the attention when each
+    runs `reps` times in a row between one event pair (h rotating over its
+    three copies, so no gate or gather launch finds its input in the
+    last-level cache), so that the event pair's own dispatch overhead, a few
+    microseconds against a gather of about 8, is spread over the launches; the
+    gaps between the kernels stay in the figure.  The attention figure is a
+    cross-check of the roofline's per-launch event pairs, which carry that
+    overhead."""
     import torch
     out = {}
-    for name, fn in (("gate", path.gate), ("gather", path.gather)):
+    for name, fn in (("gate", path.gate), ("gather", path.gather), ("attn", lambda: path.attn(0))):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         queue_ahead(torch)
         ev[0].record()
