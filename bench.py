@@ -1,11 +1,12 @@
 """Benchmark of the TokenGate gated-prefill hot path on one MI355X.
 
 A step is one pass of the whole path over one prompt of the workload:
-gate MLP over all N tokens -> top-K select (question tail kept) -> gather of
-the kept rows, gate values and positions -> for each upper layer: RoPE + the
-compact KV cache, then token-gated causal GQA attention.  Inputs are resident
-in HBM before timing starts; three copies of the hidden states rotate between
-steps so that the 256 MB last-level cache cannot serve the gate's input.
+gate MLP over all N tokens and top-K select (question tail kept) in one
+kernel -> gather of the kept rows, gate values and positions -> for each upper
+layer: RoPE + the compact KV cache, then token-gated causal GQA attention.
+Inputs are resident in HBM before timing starts; four copies of the hidden
+states rotate between steps so that the 256 MB last-level cache cannot serve
+the gate's input.
 
     python bench.py [--steps K] [--warmup W] [--workload qwen1p7b_32k]
 
@@ -42,12 +43,15 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-full-context", action="store_true",
                    help="skip the comparison of one upper layer on the K kept tokens with one on all N tokens")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the 28-layer prefill comparison (gated at layer 9 of 28 against all layers full)")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the decode attention figure over compact KV caches")
     p.add_argument("--stage-reps", type=int, default=30, help="repetitions of the per-stage timing loop")
     p.add_argument("--select", default="auto", choices=["auto", "one", "ws"],
-                   help="top-K entry point: tg_select_topk (one workgroup per prompt), tg_select_topk_ws "
-                        "(several workgroups, caller workspace), or auto: ws from %d tokens" % SELECT_WS_FROM)
+                   help="stand-alone top-K entry point timed for reference (and used by the 128k workload): "
+                        "tg_select_topk (one workgroup per prompt), tg_select_topk_ws (several workgroups, caller "
+                        "workspace), or auto: ws from %d tokens" % SELECT_WS_FROM)
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the run, launch a plain 1 GiB -> 1 GiB streaming kernel (torch.neg on fp32) "
                         "three times; its PMC byte counters calibrate FETCH_SIZE / WRITE_SIZE")
@@ -68,6 +72,9 @@ def _file_sha(path):
 SELECT_WS_FROM = 24576
 
 
+H_COPIES = 4  # copies of h: a gate input is reused only after 3 x 134 MB of other gate traffic
+
+
 class Path:
     """Device buffers and the launch sequence of one workload."""
 
@@ -76,9 +83,8 @@ class Path:
         sh = W.SHAPES[name]
         seed = W.SEEDS[name]
         self.tg, self.sh, self.dev = tg, sh, dev
-        copies = 3
         self.h = [W.hidden_states(sh.n, sh.d, sh.dtype, seed + 100 * c, planted_frac=sh.planted_frac).to(dev)
-                  for c in range(copies)]
+                  for c in range(H_COPIES)]
         w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
         self.w1, self.b1, self.w2, self.b2 = w1.to(dev), b1.to(dev), w2.to(dev), b2
         self.layers = []
@@ -91,9 +97,10 @@ class Path:
         f32, i32 = torch.float32, torch.int32
         self.g = torch.empty(sh.n, dtype=f32, device=dev)
         self.idx = torch.empty(kept, dtype=i32, device=dev)
-        self.select_ws = select == "ws" or (select == "auto" and sh.n >= SELECT_WS_FROM)
-        self.sel_workspace = (torch.empty(tg.tg_select_topk_workspace_size(sh.n), dtype=torch.uint8, device=dev)
-                              if self.select_ws else None)
+        # Zero-filled once; every call of the gate + select leaves it zero-filled.
+        self.sel_workspace = tg.select_workspace(sh.n, dev)
+        self.ref_workspace = tg.select_workspace(sh.n, dev)  # for the stand-alone select timings
+        self.ref_idx = torch.empty(kept, dtype=i32, device=dev)
         self.hk = torch.empty(kept, sh.d, dtype=sh.dtype, device=dev)
         self.gk = torch.empty(kept, dtype=f32, device=dev)
         self.pos = torch.empty(kept, dtype=i32, device=dev)
@@ -101,25 +108,41 @@ class Path:
         self.wide_g = None
         if name == "qwen1p7b_128k":  # select/attention use a widely spread gate vector
             self.wide_g = W.gate_values_wide(sh.n, seed).to(dev)
+        self.fused = self.wide_g is None
+        self.select_ws = select == "ws" or (select == "auto" and sh.n >= SELECT_WS_FROM)
         self.step_no = 0
 
-    # The five stages, each a single library call.
-    def gate(self):
-        tg = self.tg
-        h = self.h[self.step_no % len(self.h)]
-        tg.tg_gate_score(h, self.w1, self.b1, self.w2, self.b2, g=self.g)
+    def cur_h(self):
+        return self.h[self.step_no % len(self.h)]
 
-    def select(self):
-        g = self.g if self.wide_g is None else self.wide_g
-        if self.select_ws:
-            self.tg.tg_select_topk_ws(g, self.sh.k, self.sh.q_len, idx=self.idx, workspace=self.sel_workspace)
+    # The path: gate + select, gather, then per upper layer RoPE + KV and attention.
+    def prune(self):
+        """Gate and top-K select.  One kernel (tg_gate_select) where the
+        selection ranks the gate's own scores; the 128k workload ranks a drawn,
+        widely spread gate vector instead, so there the gate and the select
+        are two calls."""
+        if self.fused:
+            self.tg.tg_gate_select(self.cur_h(), self.w1, self.b1, self.w2, self.b2, self.sh.k, self.sh.q_len,
+                                   g=self.g, idx=self.idx, workspace=self.sel_workspace)
         else:
-            self.tg.tg_select_topk(g, self.sh.k, self.sh.q_len, idx=self.idx)
+            self.gate()
+            self.select(self.wide_g, self.idx)
+
+    # Stand-alone stages, timed for reference next to the fused call.
+    def gate(self):
+        self.tg.tg_gate_score(self.cur_h(), self.w1, self.b1, self.w2, self.b2, g=self.g)
+
+    def select(self, g=None, idx=None):
+        g = self.g if g is None else g
+        idx = self.ref_idx if idx is None else idx
+        if self.select_ws:
+            self.tg.tg_select_topk_ws(g, self.sh.k, self.sh.q_len, idx=idx, workspace=self.ref_workspace)
+        else:
+            self.tg.tg_select_topk(g, self.sh.k, self.sh.q_len, idx=idx)
 
     def gather(self):
         g = self.g if self.wide_g is None else self.wide_g
-        h = self.h[self.step_no % len(self.h)]
-        self.tg.tg_gather(h, g, self.idx, h_out=self.hk, g_out=self.gk, pos_out=self.pos)
+        self.tg.tg_gather(self.cur_h(), g, self.idx, h_out=self.hk, g_out=self.gk, pos_out=self.pos)
 
     def rope(self, layer):
         q, k, v, kc, vc, _ = self.layers[layer]
@@ -134,8 +157,7 @@ class Path:
             events[1].record()
 
     def step(self, attn_events=None):
-        self.gate()
-        self.select()
+        self.prune()
         self.gather()
         for layer in range(self.sh.layers):
             self.rope(layer)
@@ -160,6 +182,7 @@ def stage_bytes(sh):
     return {
         "gate": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4,
         "select": sh.n * 4 + k * 4,
+        "gate_select": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4 + k * 4,
         "gather": 2 * k * (sh.d * es + 8),
         "rope_kv": k * (2 * (sh.hq + sh.hkv) * sh.dh * es + 2 * sh.hkv * sh.dh * es + sh.dh * 4),
         "attn": k * (sh.hq * sh.dh * es * 2 + 2 * sh.hkv * sh.dh * es + 8),
@@ -214,57 +237,141 @@ def queue_ahead(torch):
         spin(SPIN_CYCLES)
 
 
+def path_stage_fns(path):
+    """(name, call) of the step's own stages, in path order (one upper layer)."""
+    first = ("gate_select", path.prune) if path.fused else ("gate", path.gate)
+    fns = [first]
+    if not path.fused:
+        fns.append(("select", lambda: path.select(path.wide_g, path.idx)))
+    fns += [("gather", path.gather), ("rope_kv", lambda: path.rope(0)), ("attn", lambda: path.attn(0))]
+    return fns
+
+
 def time_stages(path, reps):
+    """Per-stage medians (and means) in path order, each stage right after the
+    one before it, as in the step: every input the previous stage touched may
+    still sit in the last-level cache (cache-warm figures)."""
     import torch
-    sh = path.sh
-    names = ["gate", "select", "gather", "rope_kv", "attn"]
-    samples = {n: [] for n in names}
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+    fns = path_stage_fns(path)
+    samples = {n: [] for n, _ in fns}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(fns))]
     for _ in range(reps):
         queue_ahead(torch)
-        ev[0].record()
-        path.gate()
-        ev[1].record()
-        ev[2].record()
-        path.select()
-        ev[3].record()
-        ev[4].record()
-        path.gather()
-        ev[5].record()
-        ev[6].record()
-        path.rope(0)
-        ev[7].record()
-        ev[8].record()
-        path.attn(0)
-        ev[9].record()
+        for i, (_, fn) in enumerate(fns):
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
         torch.cuda.synchronize()
-        for i, n in enumerate(names):
+        for i, (n, _) in enumerate(fns):
             samples[n].append(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3)  # us
         path.step_no += 1
     return {n: statistics.median(v) for n, v in samples.items()}, {n: sum(v) / len(v) for n, v in samples.items()}
 
 
-def back_to_back(path, reps=30):
-    """Per-launch time of the gate, the gather and the attention when each
-    runs `reps` times in a row between one event pair (h rotating over its
-    three copies, so no gate or gather launch finds its input in the
-    last-level cache), so that the event pair's own dispatch overhead, a few
-    microseconds against a gather of about 8, is spread over the launches; the
-    gaps between the kernels stay in the figure.  The attention figure is a
-    cross-check of the roofline's per-launch event pairs, which carry that
-    overhead."""
+FLUSH_BYTES = 1 << 30  # written between cold launches: 4x the 256 MB last-level cache
+
+
+def cold_stages(path, reps):
+    """Per-launch event pairs of each stage after 1 GiB has been written to a
+    scratch buffer (outside the pair), so that no input is served by the L2s or
+    the 256 MB last-level cache.  The pair also holds the launch's dispatch
+    latency (a few us), so these figures are upper bounds."""
     import torch
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=path.dev)
+    fns = [(n, fn) for n, fn in path_stage_fns(path)]
+    fns += [("gate", path.gate), ("select", lambda: path.select())]
+    seen = set()
     out = {}
-    for name, fn in (("gate", path.gate), ("gather", path.gather), ("attn", lambda: path.attn(0))):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        queue_ahead(torch)
-        ev[0].record()
-        for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for n, fn in fns:
+        if n in seen:
+            continue
+        seen.add(n)
+        ts = []
+        for r in range(reps):
+            flush.fill_(float(r))
+            ev[0].record()
             fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
             path.step_no += 1
+        out[n] = statistics.median(ts)
+    del flush
+    return out
+
+
+def back_to_back(path, reps=24):
+    """Per-launch time of a stage launched `reps` times in a row between one
+    event pair, so that the pair's own dispatch overhead (a few us against a
+    gather of about 8) is spread over the launches; the gaps between the
+    kernels stay in the figure.
+
+    Cold (the HBM figures): every launch works on a footprint that was last
+    touched more than 256 MB of traffic earlier, so neither the L2s nor the
+    last-level cache can serve it:
+      gate, gate_select  the four copies of h (134 MB each) in turn;
+      gather             24 footprints: the four copies of h x six disjoint
+                         ascending sets of kept rows, each written to one of
+                         twelve output buffers in turn (16.8 MB read + 16.8 MB
+                         written per launch);
+      rope_kv            eight sets of q, k, v and caches (50 MB each) in turn.
+    Warm (no HBM claim): attention (MFMA-bound; its 50 MB of q, k, v stay in the
+    last-level cache) and the stand-alone select (128 KB of scores)."""
+    import torch
+    sh, dev, tg = path.sh, path.dev, path.tg
+    kept = min(sh.k, sh.n)
+    out = {}
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def timed(name, launches):
+        flush.fill_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for fn in launches:
+            fn()
         ev[1].record()
         torch.cuda.synchronize()
-        out[name] = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        out[name] = ev[0].elapsed_time(ev[1]) * 1e3 / len(launches)
+
+    def at(i, fn):
+        def run():
+            path.step_no = i
+            fn()
+        return run
+
+    timed("gate", [at(i, path.gate) for i in range(reps)])
+    if path.fused:
+        timed("gate_select", [at(i, path.prune) for i in range(reps)])
+    # gather: disjoint kept-row sets, each ascending, as select writes them
+    perm = torch.randperm(sh.n, generator=torch.Generator().manual_seed(5))
+    nsets = max(1, min(6, sh.n // kept))
+    sets = [perm[j * kept:(j + 1) * kept].sort().values.to(torch.int32).to(dev) for j in range(nsets)]
+    outs = [(torch.empty(kept, sh.d, dtype=sh.dtype, device=dev), torch.empty(kept, dtype=torch.float32, device=dev),
+             torch.empty(kept, dtype=torch.int32, device=dev)) for _ in range(12)]
+    g = path.g if path.wide_g is None else path.wide_g
+
+    def gather_at(i):
+        hk, gk, pos = outs[i % len(outs)]
+        return lambda: tg.tg_gather(path.h[i % len(path.h)], g, sets[(i // len(path.h)) % nsets], h_out=hk,
+                                    g_out=gk, pos_out=pos)
+
+    timed("gather", [gather_at(i) for i in range(reps)])
+    # rope + KV: eight independent sets of q, k, v and caches
+    rsets = []
+    for j in range(8):
+        q, k, v = (torch.randn(kept, hh, sh.dh, device=dev).mul_(0.09).to(sh.dtype) for hh in (sh.hq, sh.hkv, sh.hkv))
+        rsets.append((q, k, v, torch.empty_like(k), torch.empty_like(v)))
+    pos = path.pos
+
+    def rope_at(i):
+        q, k, v, kc, vc = rsets[i % len(rsets)]
+        return lambda: tg.tg_rope_kv(q, k, v, pos, path.table, k_cache=kc, v_cache=vc)
+
+    timed("rope_kv", [rope_at(i) for i in range(reps)])
+    timed("attn", [lambda: path.attn(0) for _ in range(reps)])
+    timed("select", [lambda: path.select() for _ in range(reps)])
+    del flush, rsets, outs
     return out
 
 
@@ -325,6 +432,67 @@ def upper_layer(tg, W, sh, dev, m, gated, reps=8):
     return {"rows": m, "gated": gated, "stage_us": med, "total_us": round(sum(med.values()), 2),
             "dense_us": round(dense_us, 2), "dense_TFLOP/s": round(dense_flops / (dense_us * 1e-6) / 1e12, 1),
             "attn_TFLOP/s": round(attn_flops / (med["attn"] * 1e-6) / 1e12, 1)}
+
+
+STACK_LAYERS, STACK_SELECT_LAYER = 28, 9  # Qwen3-1.7B depth; the gate sits after layer 9
+
+
+def prune_time(tg, W, sh, dev, reps=10):
+    """Median event-timed gate + select (one call) plus gather on one prompt of
+    sh.n tokens: the pruning overhead paid once per prompt at the selection
+    layer."""
+    import torch
+    seed = W.SEEDS[sh.name]
+    h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac).to(dev)
+    w1, b1, w2, b2 = (t.to(dev) if hasattr(t, "to") else t for t in W.gate_weights(sh.d, sh.hidden, sh.dtype, seed))
+    kept = min(sh.k, sh.n)
+    g = torch.empty(sh.n, dtype=torch.float32, device=dev)
+    idx = torch.empty(kept, dtype=torch.int32, device=dev)
+    ws = tg.select_workspace(sh.n, dev)
+    hk = torch.empty(kept, sh.d, dtype=sh.dtype, device=dev)
+    gk = torch.empty(kept, dtype=torch.float32, device=dev)
+    pos = torch.empty(kept, dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for r in range(reps + 2):
+        queue_ahead(torch)
+        ev[0].record()
+        tg.tg_gate_select(h, w1, b1, w2, b2, sh.k, sh.q_len, g=g, idx=idx, workspace=ws)
+        tg.tg_gather(h, g, idx, h_out=hk, g_out=gk, pos_out=pos)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    return statistics.median(ts)
+
+
+def stack_ratio(tg, W, dev):
+    """Prefill of a whole Qwen3-1.7B-shaped stack (28 layers, random weights),
+    with the gate after layer 9 and K = 4096 of N = 65536 tokens kept, against
+    the same stack with every layer on all N tokens.  Composed from medians of
+    one layer of each kind, timed separately, times the layer counts:
+        full  = 28 x (one layer on N tokens, no gate)
+        gated =  9 x (one layer on N tokens, no gate)
+               + gate + select + gather on N tokens
+               + 19 x (one gated layer on the K kept tokens)
+    Each layer is every library stage (QKV, RoPE + KV, attention, O + residual,
+    SwiGLU, down + residual); RMSNorms, embeddings and the LM head are left
+    out of both stacks."""
+    sh = W.SHAPES["stack19"]
+    full = upper_layer(tg, W, sh, dev, sh.n, gated=False, reps=2)
+    gated = upper_layer(tg, W, sh, dev, sh.k, gated=True, reps=8)
+    prune_us = prune_time(tg, W, sh, dev)
+    below = STACK_SELECT_LAYER
+    above = STACK_LAYERS - STACK_SELECT_LAYER
+    t_full = STACK_LAYERS * full["total_us"]
+    t_gated = below * full["total_us"] + prune_us + above * gated["total_us"]
+    return {"n": sh.n, "k": sh.k, "layers": STACK_LAYERS, "selection_layer": STACK_SELECT_LAYER,
+            "full_layer_us": full["total_us"], "gated_layer_us": gated["total_us"], "pruning_us": round(prune_us, 2),
+            "full_stack_ms": round(t_full / 1e3, 3), "gated_stack_ms": round(t_gated / 1e3, 3),
+            "prefill_speedup": round(t_full / t_gated, 3),
+            "composition": "per-layer medians x layer counts (9 full + pruning + 19 gated vs 28 full); "
+                           "each layer timed as one unit of six library calls",
+            "full_layer": full, "gated_layer": gated}
 
 
 def decode_step(tg, W, sh, dev, batch=32, reps=20):
@@ -616,9 +784,12 @@ def main(argv=None):
     print(f"[bench] HIP graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     med, mean = time_stages(path, args.stage_reps)
-    print(f"[bench] stage medians (us): {json.dumps({k: round(v, 2) for k, v in med.items()})}",
+    print(f"[bench] stage medians in path (us): {json.dumps({k: round(v, 2) for k, v in med.items()})}",
           file=sys.stderr, flush=True)
+    cold = cold_stages(path, max(3, args.stage_reps // 3))
     b2b = back_to_back(path)
+    print(f"[bench] cold per launch (us): {json.dumps({k: round(v, 2) for k, v in cold.items()})}; "
+          f"back to back: {json.dumps({k: round(v, 2) for k, v in b2b.items()})}", file=sys.stderr, flush=True)
     fl_attn = attn_flops(sh)
     fl_gate = gate_flops(sh)
     by = stage_bytes(sh)
@@ -635,21 +806,49 @@ def main(argv=None):
         "flops_per_launch": fl_attn,
         "avg_launch_us": round(attn_avg_us, 2),
         "launches_timed": len(attn_launch_us),
+        "duration_basis": ("avg_launch_us: mean of the HIP event pairs around every attention launch of the timed "
+                           "region (each pair also holds a few us of dispatch latency); avg_launch_us_back_to_back: "
+                           "24 launches in a row between one pair, which is what the kernel trace measures"),
+        "avg_launch_us_back_to_back": round(b2b["attn"], 2),
+        "frac_back_to_back": round(fl_attn / (b2b["attn"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
     stages = {}
-    for n in ["gate", "select", "gather", "rope_kv", "attn"]:
-        e = {"median_us": round(med[n], 2), "mean_us": round(mean[n], 2),
-             "GB/s": round(by[n] / (med[n] * 1e-6) / 1e9, 1)}
+    for n in list(med) + [x for x in ("gate", "select") if x not in med]:
+        e = {}
+        if n in med:
+            e["median_us"] = round(med[n], 2)
+            e["mean_us"] = round(mean[n], 2)
+            e["GB/s"] = round(by[n] / (med[n] * 1e-6) / 1e9, 1)
+        else:
+            e["in_path"] = False  # timed for reference only: the step runs the fused call
+        e["cold_us"] = round(cold[n], 2)
         if n in b2b:
             e["us_back_to_back"] = round(b2b[n], 2)
             e["GB/s_back_to_back"] = round(by[n] / (b2b[n] * 1e-6) / 1e9, 1)
-        if n == "gate":
-            e["TFLOP/s"] = round(fl_gate / (med[n] * 1e-6) / 1e12, 1)
+            e["back_to_back_cache"] = "warm" if n in ("attn", "select") else "cold"
+        if n in ("gate", "gate_select"):
+            e["TFLOP/s_back_to_back"] = round(fl_gate / (b2b[n] * 1e-6) / 1e12, 1)
         if n == "attn":
             e["TFLOP/s"] = round(fl_attn / (med[n] * 1e-6) / 1e12, 1)
         stages[n] = e
 
-    full = upper = None
+    def pct(name):
+        return round(100 * by[name] / (b2b[name] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)
+
+    pruning = None
+    if path.fused:
+        sel_in_gate = b2b["gate_select"] - b2b["gate"]
+        pruning = {
+            "gate_select_us": round(b2b["gate_select"], 2), "gate_us": round(b2b["gate"], 2),
+            "select_in_gate_us": round(sel_in_gate, 2), "gather_us": round(b2b["gather"], 2),
+            "select_plus_gather_us": round(sel_in_gate + b2b["gather"], 2),
+            "select_plus_gather_pct_hbm_peak": round(
+                100 * (by["select"] + by["gather"]) / ((sel_in_gate + b2b["gather"]) * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                2),
+            "basis": "back-to-back cold launches; select_in_gate = fused gate+select minus the plain gate",
+        }
+
+    full = upper = stack = None
     if not args.no_full_context:
         print("[bench] timing one upper layer on the K kept tokens and on all N tokens ...", file=sys.stderr,
               flush=True)
@@ -662,9 +861,13 @@ def main(argv=None):
         full["layer_speedup_vs_pruned"] = round(full["layer_us"] / layer_gated, 2)
         # One selection layer's overhead (gate, select, gather) is paid once per
         # prompt; every upper layer then runs on K tokens instead of N.
-        full["pruning_overhead_us"] = round(med["gate"] + med["select"] + med["gather"], 2)
+        full["pruning_overhead_us"] = round(sum(med[x] for x in med if x not in ("rope_kv", "attn")), 2)
         upper = {"ffn": FFN, "pruned": up_k, "full": up_n,
                  "layer_speedup_vs_pruned": round(up_n["total_us"] / up_k["total_us"], 2)}
+    if not args.no_stack:
+        print("[bench] timing the 28-layer stack, gated at layer 9 (N = 65536, K = 4096) ...", file=sys.stderr,
+              flush=True)
+        stack = stack_ratio(tg, W, dev)
 
     dec = None
     if not args.no_decode:
@@ -694,15 +897,20 @@ def main(argv=None):
                    "upper_layers": sh.layers, "global_batch": 1, "seq_len": sh.n},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "select_entry": "tg_select_topk_ws" if path.select_ws else "tg_select_topk",
+        "prune_entry": "tg_gate_select" if path.fused else "tg_gate_score + tg_select_topk_ws",
         "stages": stages,
+        "pruning": pruning,
         "hip_graph": graph,
         "full_context": full,
         "upper_layer": upper,
+        "stack": stack,
         "decode": dec,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
-        "gate_pct_hbm_peak": round(100 * by["gate"] / (b2b["gate"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-        "gather_pct_hbm_peak": round(100 * by["gather"] / (b2b["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        "gate_pct_hbm_peak": pct("gate"),
+        "gather_pct_hbm_peak": pct("gather"),
+        "rope_kv_pct_hbm_peak": pct("rope_kv"),
+        "hbm_pct_basis": "algorithmic bytes over back-to-back launches on footprints last touched more than 256 MB "
+                         "of traffic earlier (cold last-level cache)",
     }
     if args.copy_calibration:
         copy_calibration(torch, dev)

@@ -21,7 +21,9 @@ from .binding import (  # noqa: F401
     tg_check_positions,
     tg_decode_attn,
     tg_decode_attn_workspace_size,
+    select_workspace,
     tg_gate_score,
+    tg_gate_select,
     tg_gated_attn,
     tg_gated_attn_varlen,
     tg_gather,

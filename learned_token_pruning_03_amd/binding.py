@@ -34,6 +34,8 @@ SIGNATURES = {
     "tg_last_error": ([], ctypes.c_char_p),
     "tg_gate_score": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32,
                        _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "tg_gate_select": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32, _c_i64,
+                        _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
     "tg_select_topk": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
     "tg_select_topk_workspace_size": ([_c_i64], _c_i64),
     "tg_select_topk_ws": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
@@ -122,6 +124,22 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+# The C ABI takes raw pointers and no buffer lengths, so these checks are the
+# only guard against a call that would read or write past a tensor.
+def _vec(t: Optional[torch.Tensor], n: int, dtype: torch.dtype, name: str) -> None:
+    """t is None, or a contiguous tensor of `dtype` with at least n elements."""
+    if t is None:
+        return
+    _need(t.dtype == dtype and t.is_contiguous() and t.numel() >= n,
+          f"{name} must be a contiguous {dtype} tensor with at least {n} elements")
+
+
+def _like(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
+    """t is a contiguous tensor of exactly `shape` and `dtype`."""
+    _need(tuple(t.shape) == tuple(shape) and t.dtype == dtype and t.is_contiguous(),
+          f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 # ---------------------------------------------------------------------------
 def tg_gate_score(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
                   b2: float, g: Optional[torch.Tensor] = None, s: Optional[torch.Tensor] = None,
@@ -143,6 +161,46 @@ def tg_gate_score(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor],
     return (g, s) if want_scores or s is not None else g
 
 
+def select_workspace(n: int, device) -> torch.Tensor:
+    """A zero-filled select workspace for prompts of up to n tokens, as
+    tg_gate_select needs on first use (every call leaves it zero-filled)."""
+    return torch.zeros(max(tg_select_topk_workspace_size(n), 16), dtype=torch.uint8, device=device)
+
+
+def tg_gate_select(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor, b2: float,
+                   k: int, q_len: int, g: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, s: Optional[torch.Tensor] = None,
+                   want_scores: bool = False):
+    """Gate scores and the top-K selection over them in one call; returns
+    (g, idx), or (g, s, idx) when scores are requested.  `workspace` must be
+    a zero-filled uint8 tensor the first time it is used (select_workspace)."""
+    lib = load_library()
+    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
+    n, d = h.shape
+    hidden = w1.shape[0]
+    _need(w1.shape == (hidden, d) and w1.is_contiguous() and w1.dtype == h.dtype, "w1 must be [hidden, d]")
+    _need(w2.numel() == hidden and w2.dtype == torch.float32 and w2.is_contiguous(), "w2 must be fp32 [hidden]")
+    _need(b1 is None or (b1.numel() == hidden and b1.dtype == torch.float32 and b1.is_contiguous()),
+          "b1 must be fp32 [hidden]")
+    kept = min(int(k), n)
+    g = torch.empty(n, dtype=torch.float32, device=h.device) if g is None else g
+    idx = torch.empty(kept, dtype=torch.int32, device=h.device) if idx is None else idx
+    if want_scores and s is None:
+        s = torch.empty(n, dtype=torch.float32, device=h.device)
+    _need(g.dtype == torch.float32 and g.is_contiguous() and g.numel() >= n, "g must be contiguous fp32 [n]")
+    _need(s is None or (s.dtype == torch.float32 and s.is_contiguous() and s.numel() >= n), "s must be fp32 [n]")
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= kept,
+          "idx must be contiguous int32 with min(k, n) entries")
+    if workspace is None:
+        workspace = select_workspace(n, h.device)
+    _need(workspace.is_contiguous() and workspace.device == h.device, "workspace must be a contiguous device tensor")
+    _check("tg_gate_select",
+           lib.tg_gate_select(_dtype_code(h), n, d, hidden, _ptr(h), h.stride(0), _ptr(w1), _ptr(b1), _ptr(w2),
+                              float(b2), int(k), int(q_len), _ptr(g), _ptr(s), _ptr(idx), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(h)))
+    return (g, s, idx) if (want_scores or s is not None) else (g, idx)
+
+
 def tg_select_topk(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tensor] = None):
     """Ascending int32 indices of the min(k, n) kept tokens."""
     lib = load_library()
@@ -151,7 +209,7 @@ def tg_select_topk(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tens
     kept = min(int(k), n)
     if idx is None:
         idx = torch.empty(kept, dtype=torch.int32, device=g.device)
-    _need(idx.numel() >= kept and idx.dtype == torch.int32, "idx must be int32 with min(k, n) entries")
+    _vec(idx, kept, torch.int32, "idx")
     _check("tg_select_topk", lib.tg_select_topk(_ptr(g), n, int(k), int(q_len), _ptr(idx), _stream(g)))
     return idx
 
@@ -171,10 +229,11 @@ def tg_select_topk_ws(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.T
     kept = min(int(k), n)
     if idx is None:
         idx = torch.empty(kept, dtype=torch.int32, device=g.device)
-    _need(idx.numel() >= kept and idx.dtype == torch.int32, "idx must be int32 with min(k, n) entries")
+    _vec(idx, kept, torch.int32, "idx")
     need = tg_select_topk_workspace_size(n)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=g.device)
+    _need(workspace.is_contiguous(), "workspace must be contiguous")
     _check("tg_select_topk_ws",
            lib.tg_select_topk_ws(_ptr(g), n, int(k), int(q_len), _ptr(idx), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(g)))
@@ -184,14 +243,25 @@ def tg_select_topk_ws(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.T
 def tg_select_topk_varlen(g: torch.Tensor, cu_seqlens: torch.Tensor, q_lens: torch.Tensor, max_seqlen: int,
                           k: int, total_kept: int, idx_local: Optional[torch.Tensor] = None,
                           cu_kept: Optional[torch.Tensor] = None):
-    """Per-prompt selection over a packed score vector; returns (idx_local, cu_kept)."""
+    """Per-prompt selection over a packed score vector; returns (idx_local, cu_kept).
+
+    The kernel writes sum_b min(k, N_b) indices, which the host cannot know
+    without reading cu_seqlens; idx_local is therefore sized for the bound
+    min(batch * k, len(g)) (every prompt keeps at most k of its own tokens)."""
     lib = load_library()
+    _need(g.dim() == 1 and g.dtype == torch.float32 and g.is_contiguous(), "g must be contiguous fp32 [total]")
     batch = cu_seqlens.numel() - 1
-    _need(cu_seqlens.dtype == torch.int32 and q_lens.dtype == torch.int32, "cu_seqlens and q_lens are int32")
+    _need(batch >= 0, "cu_seqlens needs batch + 1 entries")
+    _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
+    _vec(q_lens, batch, torch.int32, "q_lens")
+    bound = min(batch * max(int(k), 0), g.numel())
+    _need(0 <= int(total_kept) <= bound, f"total_kept={total_kept} outside [0, {bound}]")
     if idx_local is None:
-        idx_local = torch.empty(max(total_kept, 1), dtype=torch.int32, device=g.device)
+        idx_local = torch.empty(max(bound, 1), dtype=torch.int32, device=g.device)
     if cu_kept is None:
         cu_kept = torch.empty(batch + 1, dtype=torch.int32, device=g.device)
+    _vec(idx_local, bound, torch.int32, "idx_local")
+    _vec(cu_kept, batch + 1, torch.int32, "cu_kept")
     _check("tg_select_topk_varlen",
            lib.tg_select_topk_varlen(_ptr(g), _ptr(cu_seqlens), _ptr(q_lens), batch, int(max_seqlen), int(k),
                                      _ptr(idx_local), _ptr(cu_kept), _stream(g)))
@@ -205,12 +275,17 @@ def tg_gather(h: torch.Tensor, g: Optional[torch.Tensor], idx: torch.Tensor, h_o
     _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
     n, d = h.shape
     nk = idx.numel()
+    _vec(idx, nk, torch.int32, "idx")
+    _vec(g, n, torch.float32, "g")
     if h_out is None:
         h_out = torch.empty(nk, d, dtype=h.dtype, device=h.device)
     if g is not None and g_out is None:
         g_out = torch.empty(nk, dtype=torch.float32, device=h.device)
     if pos_out is None:
         pos_out = torch.empty(nk, dtype=torch.int32, device=h.device)
+    _like(h_out, (nk, d), h.dtype, "h_out")
+    _vec(g_out, nk, torch.float32, "g_out")
+    _vec(pos_out, nk, torch.int32, "pos_out")
     _check("tg_gather", lib.tg_gather(_dtype_code(h), n, nk, d, _ptr(idx), _ptr(h), h.stride(0), _ptr(g),
                                       _ptr(h_out), _ptr(g_out), _ptr(pos_out), _stream(h)))
     return h_out, g_out, pos_out
@@ -219,15 +294,23 @@ def tg_gather(h: torch.Tensor, g: Optional[torch.Tensor], idx: torch.Tensor, h_o
 def tg_gather_varlen(h: torch.Tensor, g: Optional[torch.Tensor], idx_local: torch.Tensor, cu_seqlens: torch.Tensor,
                      cu_kept: torch.Tensor, max_kept: int, h_out=None, g_out=None, pos_out=None):
     lib = load_library()
+    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
     n, d = h.shape
     nk = idx_local.numel()
     batch = cu_seqlens.numel() - 1
+    _vec(idx_local, nk, torch.int32, "idx_local")
+    _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
+    _vec(cu_kept, batch + 1, torch.int32, "cu_kept")
+    _vec(g, n, torch.float32, "g")
     if h_out is None:
         h_out = torch.empty(nk, d, dtype=h.dtype, device=h.device)
     if g is not None and g_out is None:
         g_out = torch.empty(nk, dtype=torch.float32, device=h.device)
     if pos_out is None:
         pos_out = torch.empty(nk, dtype=torch.int32, device=h.device)
+    _like(h_out, (nk, d), h.dtype, "h_out")
+    _vec(g_out, nk, torch.float32, "g_out")
+    _vec(pos_out, nk, torch.int32, "pos_out")
     _check("tg_gather_varlen",
            lib.tg_gather_varlen(_dtype_code(h), _ptr(cu_seqlens), _ptr(cu_kept), batch, int(max_kept), d,
                                 _ptr(idx_local), _ptr(h), h.stride(0), _ptr(g), _ptr(h_out), _ptr(g_out),
@@ -248,18 +331,51 @@ def tg_rope_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Ten
                k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None):
     """Rotates q in place; returns (q, k_cache, v_cache)."""
     lib = load_library()
+    _need(q.dim() == 3, "q must be [n, hq, dh]")
     n, hq, dh = q.shape
-    hkv = k.shape[1]
+    hkv = k.shape[1] if k.dim() == 3 else -1
     _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
-    _need(k.shape == (n, hkv, dh) and v.shape == (n, hkv, dh), "k and v must be [n, hkv, dh]")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share a dtype")
+    _need(k.dim() == 3 and tuple(k.shape) == (n, hkv, dh) and tuple(v.shape) == (n, hkv, dh),
+          "k and v must be [n, hkv, dh]")
+    _vec(pos, n, torch.int32, "pos")
+    _need(cos_sin.dim() == 2 and cos_sin.shape[1] == dh and cos_sin.dtype == torch.float32 and
+          cos_sin.is_contiguous(), "cos_sin must be a contiguous fp32 [max_pos, dh] table")
     if k_cache is None:
         k_cache = torch.empty_like(k)
     if v_cache is None:
         v_cache = torch.empty_like(v)
+    _like(k_cache, k.shape, k.dtype, "k_cache")
+    _like(v_cache, v.shape, v.dtype, "v_cache")
     _check("tg_rope_kv", lib.tg_rope_kv(_dtype_code(q), n, hq, hkv, dh, _ptr(pos), _ptr(cos_sin),
                                         cos_sin.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
                                         _ptr(v_cache), _stream(q)))
     return q, k_cache, v_cache
+
+
+def _check_attn_operands(q, k, v, g, pos, head_gain, rows):
+    _need(q.dim() == 3 and k.dim() == 3, "q must be [n, hq, dh] and k, v [n, hkv, dh]")
+    n, hq, dh = q.shape
+    hkv = k.shape[1]
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share a dtype")
+    _need(tuple(k.shape) == (n, hkv, dh) and tuple(v.shape) == (n, hkv, dh), "k and v must be [n, hkv, dh]")
+    _vec(g, rows, torch.float32, "g")
+    _vec(pos, rows, torch.int32, "pos")
+    _need(pos is not None, "pos is required")
+    _vec(head_gain, hq, torch.float32, "head_gain")
+    return n, hq, hkv, dh
+
+
+def _attn_outputs(q, o, lse, want_lse, hq, n):
+    if o is None:
+        o = torch.empty_like(q)
+    _like(o, q.shape, q.dtype, "o")
+    if want_lse and lse is None:
+        lse = torch.empty(hq, n, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _like(lse, (hq, n), torch.float32, "lse")
+    return o, lse
 
 
 def tg_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor], pos: torch.Tensor,
@@ -271,18 +387,10 @@ def tg_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     g=None: no gate (plain causal attention).  head_gain: [hq] fp32 multiplier
     of the gate bias per query head (tg_gated_attn_ex)."""
     lib = load_library()
-    n, hq, dh = q.shape
-    hkv = k.shape[1]
-    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
-    _need((g is None or g.dtype == torch.float32) and pos.dtype == torch.int32, "g is fp32 and pos int32")
-    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
-          "head_gain is fp32 [hq]")
+    n, hq, hkv, dh = _check_attn_operands(q, k, v, g, pos, head_gain, q.shape[0] if q.dim() == 3 else 0)
     if scale is None:
         scale = dh ** -0.5
-    if o is None:
-        o = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty(hq, n, dtype=torch.float32, device=q.device)
+    o, lse = _attn_outputs(q, o, lse, want_lse, hq, n)
     if g is None or head_gain is not None:
         _check("tg_gated_attn_ex",
                lib.tg_gated_attn_ex(_dtype_code(q), None, 1, n, n, hq, hkv, dh, float(scale), _ptr(q), _ptr(k),
@@ -298,18 +406,17 @@ def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: O
                          scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
                          lse: Optional[torch.Tensor] = None, want_lse: bool = False,
                          head_gain: Optional[torch.Tensor] = None):
+    """Packed ragged batch.  max_seqlen must bound every prompt's row count
+    (cu_seqlens stays on the device, so the host does not check it)."""
     lib = load_library()
-    total, hq, dh = q.shape
-    hkv = k.shape[1]
+    total, hq, hkv, dh = _check_attn_operands(q, k, v, g, pos, head_gain, q.shape[0] if q.dim() == 3 else 0)
     batch = cu_seqlens.numel() - 1
-    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
-          "head_gain is fp32 [hq]")
+    _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
+    _need(0 <= int(max_seqlen) and (batch == 0 or int(max_seqlen) <= total or total == 0),
+          "max_seqlen must lie in [0, total rows]")
     if scale is None:
         scale = dh ** -0.5
-    if o is None:
-        o = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty(hq, total, dtype=torch.float32, device=q.device)
+    o, lse = _attn_outputs(q, o, lse, want_lse, hq, total)
     if g is None or head_gain is not None:
         _check("tg_gated_attn_ex",
                lib.tg_gated_attn_ex(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv, dh,
@@ -338,16 +445,23 @@ def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     lib = load_library()
     batch, hq, dh = q.shape
     hkv = k_cache.shape[1]
-    _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.numel() == batch + 1, "cu_seqlens is int32 [B + 1]")
+    _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
+    _need(cu_seqlens.numel() == batch + 1, "cu_seqlens is int32 [B + 1]")
+    _need(q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous(), "q and caches contiguous")
     _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and the caches share a dtype")
-    _need(head_gain is None or (head_gain.dtype == torch.float32 and head_gain.numel() == hq),
-          "head_gain is fp32 [hq]")
+    _need(k_cache.dim() == 3 and k_cache.shape[2] == dh and tuple(v_cache.shape) == tuple(k_cache.shape),
+          "k_cache and v_cache must be [total, hkv, dh]")
+    _vec(g, k_cache.shape[0], torch.float32, "g")
+    _vec(head_gain, hq, torch.float32, "head_gain")
     if scale is None:
         scale = dh ** -0.5
     if o is None:
         o = torch.empty_like(q)
+    _like(o, q.shape, q.dtype, "o")
     if want_lse and lse is None:
         lse = torch.empty(batch, hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _like(lse, (batch, hq), torch.float32, "lse")
     need = tg_decode_attn_workspace_size(batch, max_seqlen, hq, hkv, dh)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -376,7 +376,9 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
         const uint8_t* ksb = (t & 1 ? k_s1 : k_s0) + grp * KB;
         // Without a gate every tile reads the 64 zeros at the start of the table
         // (keys past the prompt are then removed by the causal test).
-        const float* bias = STREAM ? &bias_s[grp][t & 1][0] : bias_all + (has_gate ? kt * BN : 0);
+        // A prompt longer than the host's max_seqlen (a broken precondition)
+        // could reach past the table: the index is clamped into it.
+        const float* bias = STREAM ? &bias_s[grp][t & 1][0] : bias_all + (has_gate ? min(kt, MAXK / BN - 1) * BN : 0);
         bf16x8 kf[2][2][2];  // [buffer][k-step within the pair][32-key half]
         auto load_k = [&](int kp, bf16x8 (*dst)[2]) __attribute__((always_inline)) {
 #pragma unroll

@@ -17,7 +17,7 @@
 // cover the other's LDS and DMA waits.  The two partial sums meet in LDS
 // before the SiLU epilogue, which the pair also splits.  The hidden layer
 // never leaves fp32 registers.
-#include "tg_internal.h"
+#include "select_core.h"
 
 namespace tg {
 namespace {
@@ -33,11 +33,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-template <int H>
+// Selection arguments of the fused form (SEL): document length, document
+// tokens to keep, question length, output indices and the select workspace.
+struct GateSel {
+  int doc, kd, q;
+  int32_t* idx;
+  uint32_t* ws;
+};
+
+template <int H, bool SEL>
 __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int n, int d, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2, float* __restrict__ g,
-    float* __restrict__ s_out) {
+    float* __restrict__ s_out, GateSel sel) {
   constexpr int NW = kGateThreads / kWave;            // 8 waves
   constexpr int MT = 2;                               // 32-token tiles per wave
   constexpr int NT = H / 2 / 32;                      // 32-unit tiles per wave
@@ -253,13 +261,29 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
         srow[wn * 2 + kh][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = part[i][r];
   }
   __syncthreads();
-  if (tid < kGateBM) {
-    const int row = m0 + tid;
-    if (row < n) {
-      const float sc = (srow[0][tid] + srow[1][tid]) + (srow[2][tid] + srow[3][tid]) + b2;
-      g[row] = 1.0f / (1.0f + expf(-sc));
-      if (s_out) s_out[row] = sc;
-    }
+  // The ring is free from here on: the fused form counts the top digit of
+  // its document scores there.
+  SelFinishShared& ss = *reinterpret_cast<SelFinishShared*>(st0);
+  if constexpr (SEL) {
+    for (int i = tid; i < kSelBins; i += kGateThreads) ss.hist[i] = 0u;
+  }
+  float gv = 0.0f;
+  const int row = m0 + tid;
+  if (tid < kGateBM && row < n) {
+    const float sc = (srow[0][tid] + srow[1][tid]) + (srow[2][tid] + srow[3][tid]) + b2;
+    gv = 1.0f / (1.0f + expf(-sc));
+    g[row] = gv;
+    if (s_out) s_out[row] = sc;
+  }
+  if constexpr (SEL) {
+    // TokenGate paper page, Figure 1(b): the selector ranks the scores the
+    // gate just produced.  Top-digit counts of this workgroup's document
+    // tokens go to the workspace; the last workgroup to finish selects.
+    __syncthreads();
+    if (tid < kGateBM && row < sel.doc) atomicAdd(&ss.hist[order_key(gv) >> 21], 1u);
+    __syncthreads();
+    if (!sel_publish_and_arrive<kGateThreads>(ss, sel.ws)) return;
+    select_finish<kGateThreads, 64>(ss, g, sel.doc, sel.kd, sel.q, sel.idx, sel.ws);
   }
 }
 
@@ -300,28 +324,44 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
-                            const void* w1, const float* b1, const float* w2, float b2, float* g,
-                            float* s, hipStream_t stream) {
+template <bool SEL>
+static hipError_t launch_gate_any(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
+                                  const float* b1, const float* w2, float b2, float* g, float* s, GateSel sel,
+                                  hipStream_t stream) {
   if (!grid_fits((n + kGateBM - 1) / kGateBM, kGateThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n + kGateBM - 1) / kGateBM));
   const auto* hh = static_cast<const uint16_t*>(h);
   const auto* ww = static_cast<const uint16_t*>(w1);
   switch (hidden) {
     case 64:
-      hipLaunchKernelGGL(gate_bf16_kernel<64>, grid, dim3(kGateThreads), 0, stream, hh, ld_h, (int)n,
-                         d, ww, b1, w2, b2, g, s);
+      hipLaunchKernelGGL((gate_bf16_kernel<64, SEL>), grid, dim3(kGateThreads), 0, stream, hh, ld_h, (int)n, d, ww,
+                         b1, w2, b2, g, s, sel);
       break;
     case 128:
-      hipLaunchKernelGGL(gate_bf16_kernel<128>, grid, dim3(kGateThreads), 0, stream, hh, ld_h,
-                         (int)n, d, ww, b1, w2, b2, g, s);
+      hipLaunchKernelGGL((gate_bf16_kernel<128, SEL>), grid, dim3(kGateThreads), 0, stream, hh, ld_h, (int)n, d,
+                         ww, b1, w2, b2, g, s, sel);
       break;
     default:
-      hipLaunchKernelGGL(gate_bf16_kernel<256>, grid, dim3(kGateThreads), 0, stream, hh, ld_h,
-                         (int)n, d, ww, b1, w2, b2, g, s);
+      hipLaunchKernelGGL((gate_bf16_kernel<256, SEL>), grid, dim3(kGateThreads), 0, stream, hh, ld_h, (int)n, d,
+                         ww, b1, w2, b2, g, s, sel);
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
+                            const void* w1, const float* b1, const float* w2, float b2, float* g,
+                            float* s, hipStream_t stream) {
+  return launch_gate_any<false>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, GateSel{0, 0, 0, nullptr, nullptr},
+                                stream);
+}
+
+hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
+                                   const float* b1, const float* w2, float b2, float* g, float* s, int64_t k,
+                                   int64_t q_len, int32_t* idx, void* workspace, hipStream_t stream) {
+  const int64_t kept = k < n ? k : n;
+  const GateSel sel{(int)(n - q_len), (int)(kept - q_len), (int)q_len, idx, static_cast<uint32_t*>(workspace)};
+  return launch_gate_any<true>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, sel, stream);
 }
 
 hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,

@@ -64,34 +64,74 @@ TG_API const char* tg_status_string(int status) {
 TG_API const char* tg_last_error(void) { return g_last_error; }
 
 // ---------------------------------------------------------------------------
+static tg_status check_gate(const char* what, tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
+                            const void* h, int64_t ld_h, const void* w1, const float* w2, const float* g) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
+  if (n < 0 || n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "%s: n=%lld out of range", what, (long long)n);
+  if (d <= 0 || hidden <= 0) return fail(TG_ERR_INVALID_ARG, "%s: d and hidden must be positive", what);
+  if (ld_h < d) return fail(TG_ERR_INVALID_ARG, "%s: ld_h=%lld < d=%d", what, (long long)ld_h, d);
+  const int es = elem_size(dtype);
+  if ((ld_h * es) % 16 != 0) return fail(TG_ERR_INVALID_ARG, "%s: ld_h*elem_size must be a multiple of 16 bytes", what);
+  if (dtype == TG_BF16) {
+    if (d % 64 != 0) return fail(TG_ERR_UNSUPPORTED, "%s bf16: d=%d must be a multiple of 64", what, d);
+    if (hidden != 64 && hidden != 128 && hidden != 256)
+      return fail(TG_ERR_UNSUPPORTED, "%s bf16: hidden=%d must be 64, 128 or 256", what, hidden);
+  } else {
+    if (d % 4 != 0) return fail(TG_ERR_UNSUPPORTED, "%s fp32: d=%d must be a multiple of 4", what, d);
+    if (hidden > 1024) return fail(TG_ERR_UNSUPPORTED, "%s fp32: hidden=%d > 1024", what, hidden);
+  }
+  if (n == 0) return TG_OK;
+  if (!h || !w1 || !w2 || !g) return fail(TG_ERR_INVALID_ARG, "%s: NULL h, w1, w2 or g", what);
+  if (!aligned16(h) || !aligned16(w1)) return fail(TG_ERR_INVALID_ARG, "%s: h and w1 must be 16-byte aligned", what);
+  return TG_OK;
+}
+
+static hipError_t launch_gate(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden, const void* h, int64_t ld_h,
+                              const void* w1, const float* b1, const float* w2, float b2, float* g, float* s,
+                              hipStream_t stream) {
+  if (dtype == TG_BF16) return tg::launch_gate_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
+  return tg::launch_gate_f32(n, d, hidden, static_cast<const float*>(h), ld_h, static_cast<const float*>(w1), b1,
+                             w2, b2, g, s, stream);
+}
+
 TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
                                const void* h, int64_t ld_h, const void* w1, const float* b1,
                                const float* w2, float b2, float* g, float* s,
                                hipStream_t stream) {
-  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "gate: unknown dtype %d", (int)dtype);
-  if (n < 0 || n > kMaxI32) return fail(TG_ERR_INVALID_ARG, "gate: n=%lld out of range", (long long)n);
-  if (d <= 0 || hidden <= 0) return fail(TG_ERR_INVALID_ARG, "gate: d and hidden must be positive");
-  if (ld_h < d) return fail(TG_ERR_INVALID_ARG, "gate: ld_h=%lld < d=%d", (long long)ld_h, d);
-  const int es = elem_size(dtype);
-  if ((ld_h * es) % 16 != 0) return fail(TG_ERR_INVALID_ARG, "gate: ld_h*elem_size must be a multiple of 16 bytes");
-  if (dtype == TG_BF16) {
-    if (d % 64 != 0) return fail(TG_ERR_UNSUPPORTED, "gate bf16: d=%d must be a multiple of 64", d);
-    if (hidden != 64 && hidden != 128 && hidden != 256)
-      return fail(TG_ERR_UNSUPPORTED, "gate bf16: hidden=%d must be 64, 128 or 256", hidden);
-  } else {
-    if (d % 4 != 0) return fail(TG_ERR_UNSUPPORTED, "gate fp32: d=%d must be a multiple of 4", d);
-    if (hidden > 1024) return fail(TG_ERR_UNSUPPORTED, "gate fp32: hidden=%d > 1024", hidden);
-  }
+  tg_status st = check_gate("gate", dtype, n, d, hidden, h, ld_h, w1, w2, g);
+  if (st != TG_OK || n == 0) return st == TG_OK ? ok() : st;
+  return from_hip(launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream), "gate");
+}
+
+TG_API tg_status tg_gate_select(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden, const void* h, int64_t ld_h,
+                                const void* w1, const float* b1, const float* w2, float b2, int64_t k,
+                                int64_t q_len, float* g, float* s, int32_t* idx, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream) {
+  tg_status st = check_gate("gate_select", dtype, n, d, hidden, h, ld_h, w1, w2, g);
+  if (st != TG_OK) return st;
+  if (k < 0) return fail(TG_ERR_INVALID_ARG, "gate_select: k=%lld < 0", (long long)k);
+  const int64_t kept = k < n ? k : n;
+  if (q_len < 0 || q_len > kept)
+    return fail(TG_ERR_INVALID_ARG, "gate_select: q_len=%lld outside [0, min(k, n)=%lld]", (long long)q_len,
+                (long long)kept);
   if (n == 0) return ok();
-  if (!h || !w1 || !w2 || !g) return fail(TG_ERR_INVALID_ARG, "gate: NULL h, w1, w2 or g");
-  if (!aligned16(h) || !aligned16(w1)) return fail(TG_ERR_INVALID_ARG, "gate: h and w1 must be 16-byte aligned");
+  if (!idx || !workspace) return fail(TG_ERR_INVALID_ARG, "gate_select: NULL idx or workspace");
+  if (!aligned16(workspace)) return fail(TG_ERR_INVALID_ARG, "gate_select: workspace must be 16-byte aligned");
+  const int64_t need = tg::select_mw_workspace_bytes(n);
+  if (workspace_bytes < need)
+    return fail(TG_ERR_WORKSPACE, "gate_select: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  const int64_t doc = n - q_len, kd = kept - q_len;
   hipError_t e;
-  if (dtype == TG_BF16)
-    e = tg::launch_gate_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
-  else
-    e = tg::launch_gate_f32(n, d, hidden, static_cast<const float*>(h), ld_h,
-                            static_cast<const float*>(w1), b1, w2, b2, g, s, stream);
-  return from_hip(e, "gate");
+  if (dtype == TG_BF16 && kd > 0 && kd < doc) {
+    e = tg::launch_gate_select_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, k, q_len, idx, workspace, stream);
+  } else {
+    // fp32, or a budget with nothing to rank: the gate, then the selection
+    // kernel (which writes the identity or the tail directly when kd says so).
+    e = launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
+    if (e == hipSuccess) e = tg::launch_select_mw(g, n, k, q_len, idx, workspace, true, stream);
+  }
+  return from_hip(e, "gate_select");
 }
 
 // ---------------------------------------------------------------------------
@@ -129,7 +169,7 @@ TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t
   if (workspace_bytes < need)
     return fail(TG_ERR_WORKSPACE, "select_ws: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
                 (long long)need);
-  return from_hip(tg::launch_select_mw(g, n, k, q_len, idx, workspace, stream), "select_ws");
+  return from_hip(tg::launch_select_mw(g, n, k, q_len, idx, workspace, false, stream), "select_ws");
 }
 
 TG_API tg_status tg_select_topk_varlen(const float* g, const int32_t* cu_seqlens,

@@ -89,16 +89,22 @@ inline bool grid_fits(int64_t blocks_x, int threads, int64_t y = 1, int64_t z = 
 hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
                             const void* w1, const float* b1, const float* w2, float b2,
                             float* g, float* s, hipStream_t stream);
+// Gate MLP whose last workgroup also selects the top-K tokens of the scores it
+// wrote (bf16 only; workspace zero on entry, zero again on exit).  Requires
+// 0 < kd = min(k, n) - q_len < n - q_len.
+hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
+                                   const float* b1, const float* w2, float b2, float* g, float* s, int64_t k,
+                                   int64_t q_len, int32_t* idx, void* workspace, hipStream_t stream);
 hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,
                            const float* w1, const float* b1, const float* w2, float b2,
                            float* g, float* s, hipStream_t stream);
 
-// Several workgroups per prompt (select.hip); prompts above kSelectMwMaxN
-// document tokens, and the degenerate budgets, go to the one-workgroup kernel.
-constexpr int64_t kSelectMwMaxN = int64_t(1) << 24;
+// Several workgroups per prompt (select.hip), with a caller workspace of
+// select_mw_workspace_bytes(n) bytes.  ws_clean: the workspace is known to be
+// zero (as every call leaves it); otherwise a small kernel clears it first.
 int64_t select_mw_workspace_bytes(int64_t n);
 hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, void* workspace,
-                            hipStream_t stream);
+                            bool ws_clean, hipStream_t stream);
 hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len,
                          const int32_t* cu_seqlens, const int32_t* q_lens, int batch,
                          int64_t max_seqlen, int32_t* idx, int32_t* cu_kept,

@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
-    for name in ("tg_gate_score", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
+    for name in ("tg_gate_score", "tg_gate_select", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
                  "tg_select_topk_ws", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
@@ -220,7 +220,8 @@ def test_grids_beyond_one_dispatch_are_refused_before_any_hip_call(lib):
 
 def test_select_ws_validation_without_a_gpu(lib):
     ws = lib.tg_select_topk_workspace_size(32768)
-    assert ws >= (2048 + 2048 + 1024 + 16 * 2) * 4  # three histograms, two counts per 2048-key chunk
+    assert ws >= (2048 + 1) * 4  # one 11-bit histogram and an arrival counter
+    assert lib.tg_select_topk_workspace_size(1 << 30) == ws  # the same for every prompt length
     assert lib.tg_select_topk_workspace_size(-1) == -1
     ok = tg.TG_ERR_INVALID_ARG
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == tg.TG_ERR_WORKSPACE
@@ -228,3 +229,69 @@ def test_select_ws_validation_without_a_gpu(lib):
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE + 4, ws, None) == ok  # misaligned
     assert lib.tg_select_topk_ws(FAKE, 32768, 10, 11, FAKE, FAKE, ws, None) == ok  # q_len > budget
     assert lib.tg_select_topk_ws(FAKE, 0, 10, 0, FAKE, None, 0, None) == tg.TG_OK  # empty: no-op
+
+
+def test_gate_select_validation_without_a_gpu(lib):
+    """The fused gate + select checks the gate's arguments, the selection's and
+    the workspace's before any HIP call."""
+    ws = lib.tg_select_topk_workspace_size(32768)
+    E, W, U = tg.TG_ERR_INVALID_ARG, tg.TG_ERR_WORKSPACE, tg.TG_ERR_UNSUPPORTED
+
+    def call(dt=tg.TG_BF16, n=32768, d=2048, hidden=256, h=FAKE, ld=2048, w1=FAKE, w2=FAKE, k=4096, q=64, g=FAKE,
+             idx=FAKE, wsp=FAKE, wsb=ws):
+        return lib.tg_gate_select(dt, n, d, hidden, h, ld, w1, None, w2, 0.0, k, q, g, None, idx, wsp, wsb, None)
+
+    assert call(q=4097) == E and "q_len" in _err(lib)
+    assert call(k=-1) == E
+    assert call(wsb=ws - 4) == W
+    assert call(wsp=None) == E
+    assert call(wsp=FAKE + 4) == E
+    assert call(idx=None) == E
+    assert call(g=None) == E
+    assert call(hidden=100) == U
+    assert call(d=100) == U
+    assert call(h=FAKE + 2) == E
+    assert call(n=0, h=None, w1=None, w2=None, g=None, idx=None, wsp=None, k=0, q=0) == tg.TG_OK  # empty: no-op
+
+
+def test_binding_rejects_mismatched_buffers_before_any_call():
+    """The C ABI takes no buffer lengths, so the binding checks dtypes, shapes
+    and sizes itself; a mismatch raises ValueError before the library is
+    called (CPU tensors suffice: the checks come before the device check)."""
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    n, hq, hkv, dh = 8, 4, 2, 64
+    q = torch.zeros(n, hq, dh, dtype=bf)
+    k = torch.zeros(n, hkv, dh, dtype=bf)
+    pos = torch.arange(n, dtype=i32)
+    g = torch.ones(n, dtype=f32)
+    cases = [
+        lambda: tg.tg_gated_attn(q.float(), k, k, g, pos),                       # q fp32, k bf16
+        lambda: tg.tg_gated_attn(q, k[:4], k[:4], g, pos),                       # k rows < q rows
+        lambda: tg.tg_gated_attn(q, k, k, g[:4], pos),                           # g too short
+        lambda: tg.tg_gated_attn(q, k, k, g, pos.long()),                        # pos not int32
+        lambda: tg.tg_gated_attn(q, k, k, g, pos, o=torch.zeros(n, hq, dh, dtype=f32)),  # o dtype
+        lambda: tg.tg_gated_attn(q, k, k, g, pos, lse=torch.zeros(hq, n - 1)),   # lse shape
+        lambda: tg.tg_gated_attn(q, k, k, g, pos, head_gain=torch.ones(hq - 1)),  # gains per head
+        lambda: tg.tg_gated_attn_varlen(q, k, k, g, pos, torch.tensor([0, 4, 8], dtype=torch.int64), 4),
+        lambda: tg.tg_rope_kv(q, k, k, pos, torch.zeros(16, dh // 2)),           # table for another dh
+        lambda: tg.tg_rope_kv(q, k, k, pos, torch.zeros(16, dh, dtype=torch.float64)),
+        lambda: tg.tg_rope_kv(q, k, k.float(), pos, torch.zeros(16, dh)),        # v dtype
+        lambda: tg.tg_rope_kv(q, k, k, pos[:4], torch.zeros(16, dh)),           # too few positions
+        lambda: tg.tg_gather(torch.zeros(16, 64, dtype=bf), g, torch.arange(4)),  # idx int64
+        lambda: tg.tg_gather(torch.zeros(16, 64, dtype=bf), g[:4], torch.arange(4, dtype=i32)),  # g < n rows
+        lambda: tg.tg_gather(torch.zeros(16, 64, dtype=bf), None, torch.arange(4, dtype=i32),
+                             h_out=torch.zeros(3, 64, dtype=bf)),               # h_out rows
+        lambda: tg.tg_select_topk_varlen(torch.zeros(100), torch.tensor([0, 50, 100], dtype=i32),
+                                         torch.tensor([1, 1], dtype=i32), 50, 10, 21),  # total_kept > 2 x 10
+        lambda: tg.tg_select_topk_varlen(torch.zeros(100), torch.tensor([0, 50, 100], dtype=i32),
+                                         torch.tensor([1, 1], dtype=i32), 50, 10, 20,
+                                         idx_local=torch.zeros(19, dtype=i32)),  # idx_local too short
+        lambda: tg.tg_select_topk(torch.zeros(10), 5, 1, idx=torch.zeros(4, dtype=i32)),
+        lambda: tg.tg_decode_attn(q[:2], k, k, g[:4], torch.tensor([0, 4, 8], dtype=i32), 4),  # g < cache rows
+        lambda: tg.tg_decode_attn(q[:2], k, k.float(), None, torch.tensor([0, 4, 8], dtype=i32), 4),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError):
+            case()
+            pytest.fail(f"case {i} was not refused")

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_bench_prints_one_json_line_with_the_roofline(gpu_lib):
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1", "--stage-reps", "2",
-           "--no-cpu-baseline", "--no-full-context", "--no-decode"]
+           "--no-cpu-baseline", "--no-full-context", "--no-decode", "--no-stack"]
     print("running", " ".join(cmd), flush=True)
     run = subprocess.run(cmd, capture_output=True, text=True, timeout=100, cwd=ROOT)
     assert run.returncode == 0, run.stderr[-3000:]
@@ -38,8 +38,14 @@ def test_bench_prints_one_json_line_with_the_roofline(gpu_lib):
     assert abs(roof["achieved"] - roof["flops_per_launch"] / (roof["avg_launch_us"] * 1e-6) / 1e12) < 0.5
     assert roof["launches_timed"] == 3
     assert out["cpu_baseline"] is None  # switched off for this run
-    for stage in ("gate", "select", "gather", "rope_kv", "attn"):
+    for stage in ("gate_select", "gather", "rope_kv", "attn"):  # the step's own stages, in path order
         assert out["stages"][stage]["median_us"] > 0
-    for stage in ("gate", "gather"):  # also timed back to back; the HBM fractions use that figure
+    for stage in ("gate_select", "gate", "select", "gather", "rope_kv", "attn"):
+        assert out["stages"][stage]["cold_us"] > 0
         assert out["stages"][stage]["us_back_to_back"] > 0
-    assert 0 < out["gather_pct_hbm_peak"] < 100 and 0 < out["gate_pct_hbm_peak"] < 100
+    assert out["stages"]["gather"]["back_to_back_cache"] == "cold"
+    assert out["prune_entry"] == "tg_gate_select"
+    for key in ("gather_pct_hbm_peak", "gate_pct_hbm_peak", "rope_kv_pct_hbm_peak"):
+        assert 0 < out[key] < 100, key
+    assert out["pruning"]["gather_us"] > 0 and out["pruning"]["gate_select_us"] > 0
+    assert roof["avg_launch_us_back_to_back"] > 0 and 0 < roof["frac_back_to_back"] < 1

@@ -191,6 +191,107 @@ def test_select_varlen_ragged_batch(gpu_lib):
     np.testing.assert_array_equal(idx.cpu().numpy(), want)
 
 
+# ----------------------------------------------------------------------------- gate + select in one call
+def _gate_select_case(tg, h, w1, b1, w2, b2, k, q, ws=None):
+    """tg_gate_select against the plain gate on the same input (the same g, bit
+    for bit) and the oracle's selection on the g it wrote (bit-exact)."""
+    hd, w1d, b1d, w2d = h.to(DEV), w1.to(DEV), b1.to(DEV), w2.to(DEV)
+    g, idx = tg.tg_gate_select(hd, w1d, b1d, w2d, b2, k, q, workspace=ws)
+    g_plain = tg.tg_gate_score(hd, w1d, b1d, w2d, b2)
+    torch.cuda.synchronize()
+    g_cpu = g.cpu().numpy()
+    np.testing.assert_array_equal(g_cpu.view(np.uint32), g_plain.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(idx.cpu().numpy().astype(np.int64), ref_select(g_cpu, k, q))
+    return g_cpu
+
+
+@pytest.mark.parametrize("n,d,hidden,k,q,planted", [
+    (1000, 256, 64, 300, 17, 0.0), (5000, 512, 128, 999, 0, 0.05), (4097, 2048, 256, 4096, 64, 0.05),
+    (129, 64, 256, 100, 1, 0.0), (300, 2048, 256, 300, 20, 0.0), (300, 2048, 256, 1000, 20, 0.0),
+    (300, 2048, 256, 20, 20, 0.0), (3, 64, 64, 2, 1, 0.0), (40000, 256, 256, 5000, 64, 0.05),
+    (70001, 128, 256, 4096, 64, 0.05)])
+def test_gate_select_parity(gpu_lib, n, d, hidden, k, q, planted):
+    """Ragged row counts against the 128-row gate tiles, budgets that keep the
+    whole prompt or only the tail, and documents of one, two and three
+    32768-key chunks of the last workgroup's ranking."""
+    _say("gate_select", n, d, hidden, k, q)
+    h = W.hidden_states(n, d, torch.bfloat16, 31 + n, planted_frac=planted)
+    w1, b1, w2, _ = W.gate_weights(d, hidden, torch.bfloat16, 31 + n)
+    g = _gate_select_case(gpu_lib, h, w1, b1, w2, 0.25, k, q)
+    g_ref, _ = ref_gate(h, w1, b1, w2, 0.25)
+    assert _rel_err(g, g_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("b2,dup", [(0.0, 8), (40.0, 1), (-200.0, 1)])
+def test_gate_select_ties(gpu_lib, b2, dup):
+    """Equal scores: every row repeated `dup` times (equal g), or an output bias
+    that saturates the sigmoid to 1.0f, or drives it to 0 -- the lower index
+    wins every tie."""
+    n, d, hidden, k, q = 8192, 256, 256, 1000, 32
+    _say("gate_select ties", b2, dup)
+    base = W.hidden_states(n // dup, d, torch.bfloat16, 41)
+    h = base.repeat_interleave(dup, dim=0).contiguous() if dup > 1 else base
+    w1, b1, w2, _ = W.gate_weights(d, hidden, torch.bfloat16, 41)
+    g = _gate_select_case(gpu_lib, h, w1, b1, w2, b2, k, q)
+    assert len(np.unique(g)) < n  # ties present
+
+
+def test_gate_select_reuses_its_workspace(gpu_lib):
+    """One workspace across calls of different lengths and budgets: each call
+    leaves it zero-filled, as the next one needs."""
+    _say("gate_select workspace reuse")
+    ws = gpu_lib.select_workspace(50000, DEV)
+    for n, d, k, q, seed in [(40000, 256, 5000, 64, 1), (1000, 128, 300, 8, 2), (32768, 2048, 4096, 64, 3),
+                             (2048, 64, 2048, 16, 4), (9000, 256, 77, 5, 5)]:
+        h = W.hidden_states(n, d, torch.bfloat16, seed, planted_frac=0.05)
+        w1, b1, w2, _ = W.gate_weights(d, 256, torch.bfloat16, seed)
+        _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+
+
+def test_gate_select_recounts_a_histogram_that_does_not_add_up(gpu_lib):
+    """A workspace whose histogram holds stale counts (arrival counter zero):
+    the last workgroup finds that the counts do not add up to the document
+    length, counts the keys itself, and still selects exactly."""
+    _say("gate_select stale histogram")
+    ws = gpu_lib.select_workspace(20000, DEV)
+    ws[:8192] = 7  # stale histogram words; the counter (word 2048, bytes 8192..8195) stays zero
+    n, d, k, q = 20000, 256, 3000, 40
+    h = W.hidden_states(n, d, torch.bfloat16, 51, planted_frac=0.05)
+    w1, b1, w2, _ = W.gate_weights(d, 256, torch.bfloat16, 51)
+    _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_gate_select_fp32_tiny(gpu_lib):
+    sh = W.SHAPES["tiny"]
+    _say("gate_select tiny fp32")
+    h = W.hidden_states(sh.n, sh.d, torch.float32, W.SEEDS["tiny"])
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, torch.float32, W.SEEDS["tiny"])
+    g = _gate_select_case(gpu_lib, h, w1, b1, w2, b2, sh.k, sh.q_len)
+    g_ref, _ = ref_gate(h, w1, b1, w2, b2)
+    assert _rel_err(g, g_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["qwen1p7b_32k", "stack19", "qwen1p7b_128k"])
+def test_gate_select_full_sizes(gpu_lib, name):
+    """The bench workloads' gate + select at full size: g on every row within
+    1e-2 of the oracle's gate (so the 131072-token gate, 1024 workgroups, is
+    checked too), idx bit-exact on the g the call wrote."""
+    sh = W.SHAPES[name]
+    seed = W.SEEDS[name]
+    _say("gate_select full size", name, sh.n, sh.k)
+    h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac)
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+    g = _gate_select_case(gpu_lib, h, w1, b1, w2, b2, sh.k, sh.q_len)
+    g_ref, _ = ref_gate(h, w1, b1, w2, b2)
+    err = _rel_err(g, g_ref)
+    _say("  max rel err g", err)
+    assert err <= 1e-2
+
+
 # ----------------------------------------------------------------------------- gather
 @pytest.mark.parametrize("dtype,n,d,nk", [(torch.bfloat16, 1000, 2048, 333), (torch.float32, 512, 256, 128),
                                           (torch.bfloat16, 32768, 2048, 4096), (torch.bfloat16, 50, 8, 50)])
