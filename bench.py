@@ -115,18 +115,25 @@ class Path:
     def cur_h(self):
         return self.h[self.step_no % len(self.h)]
 
-    # The path: gate + select, gather, then per upper layer RoPE + KV and attention.
+    # The path: gate + select + gather, then per upper layer RoPE + KV and attention.
     def prune(self):
-        """Gate and top-K select.  One kernel (tg_gate_select) where the
-        selection ranks the gate's own scores; the 128k workload ranks a drawn,
-        widely spread gate vector instead, so there the gate and the select
-        are two calls."""
+        """Gate, top-K select and gather.  Two kernels (tg_gate_select_gather)
+        where the selection ranks the gate's own scores; the 128k workload
+        ranks a drawn, widely spread gate vector instead, so there the gate,
+        the select and the gather are three calls."""
         if self.fused:
-            self.tg.tg_gate_select(self.cur_h(), self.w1, self.b1, self.w2, self.b2, self.sh.k, self.sh.q_len,
-                                   g=self.g, idx=self.idx, workspace=self.sel_workspace)
+            self.tg.tg_gate_select_gather(self.cur_h(), self.w1, self.b1, self.w2, self.b2, self.sh.k,
+                                          self.sh.q_len, g=self.g, idx=self.idx, h_out=self.hk, g_out=self.gk,
+                                          pos_out=self.pos, workspace=self.sel_workspace)
         else:
             self.gate()
             self.select(self.wide_g, self.idx)
+            self.gather()
+
+    def gate_select(self):
+        """Gate + select without the gather (reference timing)."""
+        self.tg.tg_gate_select(self.cur_h(), self.w1, self.b1, self.w2, self.b2, self.sh.k, self.sh.q_len,
+                               g=self.g, idx=self.idx, workspace=self.sel_workspace)
 
     # Stand-alone stages, timed for reference next to the fused call.
     def gate(self):
@@ -158,7 +165,6 @@ class Path:
 
     def step(self, attn_events=None):
         self.prune()
-        self.gather()
         for layer in range(self.sh.layers):
             self.rope(layer)
             self.attn(layer, None if attn_events is None else attn_events[layer])
@@ -183,6 +189,7 @@ def stage_bytes(sh):
         "gate": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4,
         "select": sh.n * 4 + k * 4,
         "gate_select": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4 + k * 4,
+        "prune": sh.n * sh.d * es + sh.hidden * sh.d * es + sh.n * 4 + k * 4 + 2 * k * (sh.d * es + 8),
         "gather": 2 * k * (sh.d * es + 8),
         "rope_kv": k * (2 * (sh.hq + sh.hkv) * sh.dh * es + 2 * sh.hkv * sh.dh * es + sh.dh * 4),
         "attn": k * (sh.hq * sh.dh * es * 2 + 2 * sh.hkv * sh.dh * es + 8),
@@ -239,12 +246,17 @@ def queue_ahead(torch):
 
 def path_stage_fns(path):
     """(name, call) of the step's own stages, in path order (one upper layer)."""
-    first = ("gate_select", path.prune) if path.fused else ("gate", path.gate)
-    fns = [first]
-    if not path.fused:
-        fns.append(("select", lambda: path.select(path.wide_g, path.idx)))
-    fns += [("gather", path.gather), ("rope_kv", lambda: path.rope(0)), ("attn", lambda: path.attn(0))]
-    return fns
+    if path.fused:
+        fns = [("prune", path.prune)]
+    else:
+        fns = [("gate", path.gate), ("select", lambda: path.select(path.wide_g, path.idx)), ("gather", path.gather)]
+    return fns + [("rope_kv", lambda: path.rope(0)), ("attn", lambda: path.attn(0))]
+
+
+def reference_fns(path):
+    """Stand-alone calls timed for reference next to the step's own stages."""
+    return [("gate", path.gate), ("gate_select", path.gate_select), ("select", lambda: path.select()),
+            ("gather", path.gather)]
 
 
 def time_stages(path, reps):
@@ -278,8 +290,7 @@ def cold_stages(path, reps):
     latency (a few us), so these figures are upper bounds."""
     import torch
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=path.dev)
-    fns = [(n, fn) for n, fn in path_stage_fns(path)]
-    fns += [("gate", path.gate), ("select", lambda: path.select())]
+    fns = path_stage_fns(path) + reference_fns(path)
     seen = set()
     out = {}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -310,7 +321,8 @@ def back_to_back(path, reps=24):
     Cold (the HBM figures): every launch works on a footprint that was last
     touched more than 256 MB of traffic earlier, so neither the L2s nor the
     last-level cache can serve it:
-      gate, gate_select  the four copies of h (134 MB each) in turn;
+      gate, gate_select, prune (gate + select + gather)
+                         the four copies of h (134 MB each) in turn;
       gather             24 footprints: the four copies of h x six disjoint
                          ascending sets of kept rows, each written to one of
                          twelve output buffers in turn (16.8 MB read + 16.8 MB
@@ -342,7 +354,8 @@ def back_to_back(path, reps=24):
 
     timed("gate", [at(i, path.gate) for i in range(reps)])
     if path.fused:
-        timed("gate_select", [at(i, path.prune) for i in range(reps)])
+        timed("prune", [at(i, path.prune) for i in range(reps)])
+        timed("gate_select", [at(i, path.gate_select) for i in range(reps)])
     # gather: disjoint kept-row sets, each ascending, as select writes them
     perm = torch.randperm(sh.n, generator=torch.Generator().manual_seed(5))
     nsets = max(1, min(6, sh.n // kept))
@@ -813,7 +826,7 @@ def main(argv=None):
         "frac_back_to_back": round(fl_attn / (b2b["attn"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
     stages = {}
-    for n in list(med) + [x for x in ("gate", "select") if x not in med]:
+    for n in list(med) + [x for x, _ in reference_fns(path) if x not in med]:
         e = {}
         if n in med:
             e["median_us"] = round(med[n], 2)
@@ -826,7 +839,7 @@ def main(argv=None):
             e["us_back_to_back"] = round(b2b[n], 2)
             e["GB/s_back_to_back"] = round(by[n] / (b2b[n] * 1e-6) / 1e9, 1)
             e["back_to_back_cache"] = "warm" if n in ("attn", "select") else "cold"
-        if n in ("gate", "gate_select"):
+        if n in ("gate", "gate_select", "prune") and n in b2b:
             e["TFLOP/s_back_to_back"] = round(fl_gate / (b2b[n] * 1e-6) / 1e12, 1)
         if n == "attn":
             e["TFLOP/s"] = round(fl_attn / (med[n] * 1e-6) / 1e12, 1)
@@ -837,17 +850,21 @@ def main(argv=None):
 
     pruning = None
     if path.fused:
-        sel_in_gate = b2b["gate_select"] - b2b["gate"]
+        # The gate's own time (the plain gate kernel, same grid and main loop)
+        # is taken out of the fused call: what is left is the ranking in the
+        # gate's last workgroup plus the compaction-and-gather kernel.
+        sel_gather = b2b["prune"] - b2b["gate"]
         pruning = {
-            "gate_select_us": round(b2b["gate_select"], 2), "gate_us": round(b2b["gate"], 2),
-            "select_in_gate_us": round(sel_in_gate, 2), "gather_us": round(b2b["gather"], 2),
-            "select_plus_gather_us": round(sel_in_gate + b2b["gather"], 2),
+            "prune_us": round(b2b["prune"], 2), "gate_us": round(b2b["gate"], 2),
+            "gate_select_us": round(b2b["gate_select"], 2),
+            "select_plus_gather_us": round(sel_gather, 2),
+            "select_plus_gather_GB/s": round((by["select"] + by["gather"]) / (sel_gather * 1e-6) / 1e9, 1),
             "select_plus_gather_pct_hbm_peak": round(
-                100 * (by["select"] + by["gather"]) / ((sel_in_gate + b2b["gather"]) * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                2),
-            "basis": "back-to-back cold launches; select_in_gate = fused gate+select minus the plain gate",
+                100 * (by["select"] + by["gather"]) / (sel_gather * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "standalone_gather_us": round(b2b["gather"], 2),
+            "basis": "back-to-back launches on cold footprints; select_plus_gather = tg_gate_select_gather minus "
+                     "the plain gate (the ranking in the gate's last workgroup plus the compaction + gather kernel)",
         }
-
     full = upper = stack = None
     if not args.no_full_context:
         print("[bench] timing one upper layer on the K kept tokens and on all N tokens ...", file=sys.stderr,
@@ -897,7 +914,7 @@ def main(argv=None):
                    "upper_layers": sh.layers, "global_batch": 1, "seq_len": sh.n},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "prune_entry": "tg_gate_select" if path.fused else "tg_gate_score + tg_select_topk_ws",
+        "prune_entry": "tg_gate_select_gather" if path.fused else "tg_gate_score + tg_select_topk_ws + tg_gather",
         "stages": stages,
         "pruning": pruning,
         "hip_graph": graph,

@@ -136,16 +136,16 @@ TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hid
 TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_len,
                                 int32_t* idx, hipStream_t stream);
 
-/* The same selection (same arguments, same output, bit for bit) spread over
- * ceil((n - q_len) / 4096) workgroups, for prompts long enough that one
- * workgroup's radix passes dominate the path.  Every workgroup counts the top
- * 11 bits of its 4096 keys; the last one to finish (an arrival counter in the
- * workspace, no waiting) ranks the rest alone.  It takes a caller workspace
- * of at least tg_select_topk_workspace_size(n) bytes (8448 for every n),
- * 16-byte aligned, whose contents need not be initialised: a small kernel
- * clears it first, so a call is two kernels.  Calls that share a workspace
- * must be ordered on one stream.  Budgets that keep the whole document or none
- * of it run the one-workgroup kernel of tg_select_topk instead.
+/* The same selection (same arguments, same output, bit for bit) in three
+ * short kernels: a clear of the workspace's counts; ceil((n - q_len) / 4096)
+ * workgroups that count the top 11 bits of their keys, the last of which to
+ * finish (an arrival counter in the workspace, no waiting) ranks alone; and
+ * one workgroup per 64 tokens that writes the kept indices.  It takes a
+ * caller workspace of at least tg_select_topk_workspace_size(n) bytes
+ * (8448 + 12 ceil(n / 64) + 4 ceil(n / 8)), 16-byte aligned, whose contents
+ * need not be initialised.  Calls that share a workspace must be ordered on one stream.
+ * Budgets that keep the whole document or none of it run the one-workgroup
+ * kernel of tg_select_topk instead.
  * Errors: as tg_select_topk; a NULL or misaligned workspace -> INVALID_ARG;
  * a workspace smaller than tg_select_topk_workspace_size(n) -> WORKSPACE. */
 TG_API int64_t tg_select_topk_workspace_size(int64_t n); /* -1 for n outside [0, 2^31) */
@@ -153,25 +153,28 @@ TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t
                                    int32_t* idx, void* workspace, int64_t workspace_bytes,
                                    hipStream_t stream);
 
-/* Stages 1 and 2 in one kernel: tg_gate_score over the n tokens, then
+/* Stages 1 and 2 in two kernels: tg_gate_score over the n tokens, then
  * tg_select_topk over the scores it wrote.  [paper] Figure 1(b): the selector
  * ranks the importance scores of the gate module at layer L.  Each
  * workgroup of the gate counts the top 11 bits of its document scores into
- * the workspace; the last workgroup to finish ranks every score and writes
+ * the workspace; the last workgroup to finish ranks every score (the kd-th
+ * largest key, how many keys equal to it are kept, and the counts before
+ * every 64-token chunk); a second kernel, one workgroup per 64 tokens, writes
  * idx.  The outputs equal those of tg_gate_score followed by tg_select_topk
  * on the g this call writes (bit for bit for idx).
  *
  *   Arguments as tg_gate_score, plus k, q_len, idx as tg_select_topk.
  *   workspace  at least tg_select_topk_workspace_size(n) bytes, 16-byte
  *              aligned, ZERO-FILLED before its first use (e.g. allocated
- *              zeroed); every call leaves it zero-filled again, so a caller
- *              reuses it across calls with no clearing.  It holds a histogram
- *              and an arrival counter.  A histogram that does not add up
- *              makes the call count the keys again (slower, same result);
- *              a non-zero counter on entry (memory that is neither fresh
- *              zeros nor left by a previous call) gives undefined indices.
- *              Calls sharing a workspace must be ordered on one stream.
- *   dtype      TG_BF16 runs the fused kernel; TG_FP32 runs the fp32 gate
+ *              zeroed).  Every call leaves its counts and arrival counter
+ *              (the first 8196 bytes) zero again, so a caller reuses it
+ *              across calls with no clearing.  Counts that do not add up make
+ *              the call count the keys again (slower, same result); a non-zero
+ *              counter on entry (memory that is neither fresh zeros nor left by
+ *              a previous call) gives undefined indices, never an access
+ *              outside the arguments.  Calls sharing a workspace must be
+ *              ordered on one stream.
+ *   dtype      TG_BF16 runs the fused kernels; TG_FP32 runs the fp32 gate
  *              followed by the multi-workgroup selection (same workspace).
  * Errors: those of tg_gate_score and tg_select_topk_ws.
  */
@@ -180,6 +183,25 @@ TG_API tg_status tg_gate_select(tg_dtype dtype, int64_t n, int32_t d, int32_t hi
                                 const float* w2, float b2, int64_t k, int64_t q_len,
                                 float* g, float* s, int32_t* idx, void* workspace,
                                 int64_t workspace_bytes, hipStream_t stream);
+
+/* Stages 1 to 3 in two kernels: tg_gate_select, with the kernel that places
+ * the kept tokens also copying them: h_out[i] = h[idx[i]], g_out[i] =
+ * g[idx[i]], pos_out[i] = idx[i] (tg_gather's outputs, bit for bit).  The
+ * ranking lists the kept tokens as items of at most 8 rows (a 64-token
+ * chunk with many kept tokens gives several items), one workgroup each, so
+ * the copy stays balanced however the kept tokens cluster.
+ * [paper] Figure 1(b): the selector forwards the kept hidden states together
+ * with their importance scores.
+ *   h_out    [min(k, n), d] contiguous, 16-byte aligned (not NULL).
+ *   g_out    [min(k, n)] fp32, or NULL.   pos_out [min(k, n)] int32, or NULL.
+ * Other arguments, workspace rules and errors as tg_gate_select. */
+TG_API tg_status tg_gate_select_gather(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
+                                       const void* h, int64_t ld_h, const void* w1,
+                                       const float* b1, const float* w2, float b2, int64_t k,
+                                       int64_t q_len, float* g, float* s, int32_t* idx,
+                                       void* h_out, float* g_out, int32_t* pos_out,
+                                       void* workspace, int64_t workspace_bytes,
+                                       hipStream_t stream);
 
 /* Ragged batch of prompts packed along the token axis.
  *   g           [total] fp32, prompt b occupies [cu_seqlens[b], cu_seqlens[b+1]).

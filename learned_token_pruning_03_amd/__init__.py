@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     select_workspace,
     tg_gate_score,
     tg_gate_select,
+    tg_gate_select_gather,
     tg_gated_attn,
     tg_gated_attn_varlen,
     tg_gather,

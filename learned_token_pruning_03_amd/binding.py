@@ -36,6 +36,9 @@ SIGNATURES = {
                        _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_gate_select": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32, _c_i64,
                         _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
+    "tg_gate_select_gather": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_f32,
+                               _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp],
+                              ctypes.c_int),
     "tg_select_topk": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
     "tg_select_topk_workspace_size": ([_c_i64], _c_i64),
     "tg_select_topk_ws": ([_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
@@ -167,6 +170,17 @@ def select_workspace(n: int, device) -> torch.Tensor:
     return torch.zeros(max(tg_select_topk_workspace_size(n), 16), dtype=torch.uint8, device=device)
 
 
+def _check_gate_inputs(h, w1, b1, w2):
+    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
+    n, d = h.shape
+    hidden = w1.shape[0]
+    _need(w1.shape == (hidden, d) and w1.is_contiguous() and w1.dtype == h.dtype, "w1 must be [hidden, d]")
+    _need(w2.numel() == hidden and w2.dtype == torch.float32 and w2.is_contiguous(), "w2 must be fp32 [hidden]")
+    _need(b1 is None or (b1.numel() == hidden and b1.dtype == torch.float32 and b1.is_contiguous()),
+          "b1 must be fp32 [hidden]")
+    return n, d, hidden
+
+
 def tg_gate_select(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor, b2: float,
                    k: int, q_len: int, g: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, s: Optional[torch.Tensor] = None,
@@ -175,22 +189,15 @@ def tg_gate_select(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor]
     (g, idx), or (g, s, idx) when scores are requested.  `workspace` must be
     a zero-filled uint8 tensor the first time it is used (select_workspace)."""
     lib = load_library()
-    _need(h.dim() == 2 and h.stride(1) == 1, "h must be [n, d] with unit column stride")
-    n, d = h.shape
-    hidden = w1.shape[0]
-    _need(w1.shape == (hidden, d) and w1.is_contiguous() and w1.dtype == h.dtype, "w1 must be [hidden, d]")
-    _need(w2.numel() == hidden and w2.dtype == torch.float32 and w2.is_contiguous(), "w2 must be fp32 [hidden]")
-    _need(b1 is None or (b1.numel() == hidden and b1.dtype == torch.float32 and b1.is_contiguous()),
-          "b1 must be fp32 [hidden]")
+    n, d, hidden = _check_gate_inputs(h, w1, b1, w2)
     kept = min(int(k), n)
     g = torch.empty(n, dtype=torch.float32, device=h.device) if g is None else g
     idx = torch.empty(kept, dtype=torch.int32, device=h.device) if idx is None else idx
     if want_scores and s is None:
         s = torch.empty(n, dtype=torch.float32, device=h.device)
-    _need(g.dtype == torch.float32 and g.is_contiguous() and g.numel() >= n, "g must be contiguous fp32 [n]")
-    _need(s is None or (s.dtype == torch.float32 and s.is_contiguous() and s.numel() >= n), "s must be fp32 [n]")
-    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= kept,
-          "idx must be contiguous int32 with min(k, n) entries")
+    _vec(g, n, torch.float32, "g")
+    _vec(s, n, torch.float32, "s")
+    _vec(idx, kept, torch.int32, "idx")
     if workspace is None:
         workspace = select_workspace(n, h.device)
     _need(workspace.is_contiguous() and workspace.device == h.device, "workspace must be a contiguous device tensor")
@@ -199,6 +206,38 @@ def tg_gate_select(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor]
                               float(b2), int(k), int(q_len), _ptr(g), _ptr(s), _ptr(idx), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(h)))
     return (g, s, idx) if (want_scores or s is not None) else (g, idx)
+
+
+def tg_gate_select_gather(h: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                          b2: float, k: int, q_len: int, g: Optional[torch.Tensor] = None,
+                          idx: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
+                          g_out: Optional[torch.Tensor] = None, pos_out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """Gate, top-K select and gather of the kept rows in two kernels; returns
+    (g, idx, h_out, g_out, pos_out).  Workspace as tg_gate_select."""
+    lib = load_library()
+    n, d, hidden = _check_gate_inputs(h, w1, b1, w2)
+    kept = min(int(k), n)
+    dev = h.device
+    g = torch.empty(n, dtype=torch.float32, device=dev) if g is None else g
+    idx = torch.empty(kept, dtype=torch.int32, device=dev) if idx is None else idx
+    h_out = torch.empty(kept, d, dtype=h.dtype, device=dev) if h_out is None else h_out
+    g_out = torch.empty(kept, dtype=torch.float32, device=dev) if g_out is None else g_out
+    pos_out = torch.empty(kept, dtype=torch.int32, device=dev) if pos_out is None else pos_out
+    _vec(g, n, torch.float32, "g")
+    _vec(idx, kept, torch.int32, "idx")
+    _like(h_out, (kept, d), h.dtype, "h_out")
+    _vec(g_out, kept, torch.float32, "g_out")
+    _vec(pos_out, kept, torch.int32, "pos_out")
+    if workspace is None:
+        workspace = select_workspace(n, dev)
+    _need(workspace.is_contiguous() and workspace.device == dev, "workspace must be a contiguous device tensor")
+    _check("tg_gate_select_gather",
+           lib.tg_gate_select_gather(_dtype_code(h), n, d, hidden, _ptr(h), h.stride(0), _ptr(w1), _ptr(b1),
+                                     _ptr(w2), float(b2), int(k), int(q_len), _ptr(g), None, _ptr(idx), _ptr(h_out),
+                                     _ptr(g_out), _ptr(pos_out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(h)))
+    return g, idx, h_out, g_out, pos_out
 
 
 def tg_select_topk(g: torch.Tensor, k: int, q_len: int, idx: Optional[torch.Tensor] = None):

@@ -17,6 +17,8 @@
 // cover the other's LDS and DMA waits.  The two partial sums meet in LDS
 // before the SiLU epilogue, which the pair also splits.  The hidden layer
 // never leaves fp32 registers.
+#include <type_traits>
+
 #include "select_core.h"
 
 namespace tg {
@@ -34,10 +36,9 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // Selection arguments of the fused form (SEL): document length, document
-// tokens to keep, question length, output indices and the select workspace.
+// tokens to keep and the select workspace.
 struct GateSel {
-  int doc, kd, q;
-  int32_t* idx;
+  int doc, kd;
   uint32_t* ws;
 };
 
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
   __shared__ float srow[4][kGateBM];
+  // Ranking state of the fused form (the keys themselves go to the ring).
+  __shared__ std::conditional_t<SEL, SelFinishShared, char> sel_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,18 +264,18 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
         srow[wn * 2 + kh][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = part[i][r];
   }
   __syncthreads();
-  // The ring is free from here on: the fused form counts the top digit of
-  // its document scores there.
-  SelFinishShared& ss = *reinterpret_cast<SelFinishShared*>(st0);
   if constexpr (SEL) {
-    for (int i = tid; i < kSelBins; i += kGateThreads) ss.hist[i] = 0u;
+    for (int i = tid; i < kSelBins; i += kGateThreads) sel_sh.hist[i] = 0u;
   }
   float gv = 0.0f;
   const int row = m0 + tid;
   if (tid < kGateBM && row < n) {
     const float sc = (srow[0][tid] + srow[1][tid]) + (srow[2][tid] + srow[3][tid]) + b2;
     gv = 1.0f / (1.0f + expf(-sc));
-    g[row] = gv;
+    if constexpr (SEL)  // read back in this kernel by the last workgroup: written past the L2
+      __hip_atomic_store(&g[row], gv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      g[row] = gv;
     if (s_out) s_out[row] = sc;
   }
   if constexpr (SEL) {
@@ -280,10 +283,21 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     // gate just produced.  Top-digit counts of this workgroup's document
     // tokens go to the workspace; the last workgroup to finish selects.
     __syncthreads();
-    if (tid < kGateBM && row < sel.doc) atomicAdd(&ss.hist[order_key(gv) >> 21], 1u);
+    if (tid < kGateBM && row < sel.doc) atomicAdd(&sel_sh.hist[order_key(gv) >> 21], 1u);
     __syncthreads();
-    if (!sel_publish_and_arrive<kGateThreads>(ss, sel.ws)) return;
-    select_finish<kGateThreads, 64>(ss, g, sel.doc, sel.kd, sel.q, sel.idx, sel.ws);
+    if (!sel_publish_and_arrive<kGateThreads, true>(sel_sh, sel.ws)) return;
+    // The ring is free: its three stages hold the keys while the last
+    // workgroup ranks.
+    constexpr int kPage = STAGE / 4 / kCompactChunk * kCompactChunk;
+    constexpr int kBlockTok = (3 * kPage < kSelMaxBlockChunks * kCompactChunk ? 3 * kPage
+                                                                             : kSelMaxBlockChunks * kCompactChunk);
+    SelKeys kp;
+    kp.page[0] = reinterpret_cast<uint32_t*>(st0);
+    kp.page[1] = reinterpret_cast<uint32_t*>(st1);
+    kp.page[2] = reinterpret_cast<uint32_t*>(st2);
+    kp.page_tokens = kPage;
+    kp.block_tokens = kBlockTok;
+    select_finish<kGateThreads>(sel_sh, kp, g, sel.doc, sel.kd, sel.ws);
   }
 }
 
@@ -352,16 +366,18 @@ static hipError_t launch_gate_any(int64_t n, int d, int hidden, const void* h, i
 hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
                             const void* w1, const float* b1, const float* w2, float b2, float* g,
                             float* s, hipStream_t stream) {
-  return launch_gate_any<false>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, GateSel{0, 0, 0, nullptr, nullptr},
-                                stream);
+  return launch_gate_any<false>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, GateSel{0, 0, nullptr}, stream);
 }
 
 hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
                                    const float* b1, const float* w2, float b2, float* g, float* s, int64_t k,
-                                   int64_t q_len, int32_t* idx, void* workspace, hipStream_t stream) {
+                                   int64_t q_len, int32_t* idx, void* workspace, void* h_out, float* g_out,
+                                   int32_t* pos_out, hipStream_t stream) {
   const int64_t kept = k < n ? k : n;
-  const GateSel sel{(int)(n - q_len), (int)(kept - q_len), (int)q_len, idx, static_cast<uint32_t*>(workspace)};
-  return launch_gate_any<true>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, sel, stream);
+  const GateSel sel{(int)(n - q_len), (int)(kept - q_len), static_cast<uint32_t*>(workspace)};
+  hipError_t e = launch_gate_any<true>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, sel, stream);
+  if (e != hipSuccess) return e;
+  return launch_compact(g, n, k, q_len, idx, workspace, h, ld_h * 2, d * 2, h_out, g_out, pos_out, stream);
 }
 
 hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,

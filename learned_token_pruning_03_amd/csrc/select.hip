@@ -290,39 +290,188 @@ void launch_kpt(const float* g, int n, int64_t k, int q, const int32_t* cu, cons
 }
 
 // ---- several workgroups per prompt ------------------------------------------
-// The same selection with the top digit counted by ceil(doc / 4096)
-// workgroups of 1024 threads (4 keys each) in LDS, then added to the
-// workspace histogram with device atomics.  The last workgroup to arrive
-// finishes the selection alone (select_finish): no grid-wide barrier and no
-// waiting, so every workgroup runs to its end whatever the dispatch order.
-constexpr int kHistThreads = 1024;
-constexpr int kHistKpt = 4;
+// The same selection in three short kernels with no grid-wide barrier:
+//   sel_clear_kernel        zeroes the workspace's histogram and counter;
+//   sel_hist_finish_kernel  ceil(doc / 4096) workgroups of 512 threads count
+//                           the top 11 bits of 8 keys per thread in LDS and
+//                           add them to the workspace; the last workgroup to
+//                           arrive ranks alone (select_finish): T, need and
+//                           the counts before every 64-token chunk;
+//   compact_kernel          one workgroup per 64-token chunk writes the kept
+//                           indices of its chunk.
+// No workgroup ever waits for another, whatever the dispatch order.
+constexpr int kHistThreads = 512;
+constexpr int kHistKpt = 8;
 constexpr int kHistChunk = kHistThreads * kHistKpt;
 
 __global__ __launch_bounds__(256) void sel_clear_kernel(uint32_t* __restrict__ ws) {
-  for (int i = threadIdx.x; i < kSelWsWords; i += 256) ws[i] = 0u;
+  for (int i = threadIdx.x; i <= kSelWsCounter; i += 256) ws[i] = 0u;
 }
 
-template <int KPT_FIN>
+constexpr int kFinishBlock = kSelMaxBlockChunks * kCompactChunk;  // keys the last workgroup holds in LDS
+
 __global__ __launch_bounds__(kHistThreads) void sel_hist_finish_kernel(const float* __restrict__ g, int doc, int kd,
-                                                                       int q, int32_t* __restrict__ out,
                                                                        uint32_t* __restrict__ ws) {
   __shared__ SelFinishShared sh;
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kFinishBlock];
   for (int i = threadIdx.x; i < kSelBins; i += kHistThreads) sh.hist[i] = 0u;
   __syncthreads();
   const int base = blockIdx.x * kHistChunk + threadIdx.x * kHistKpt;
   if (base + kHistKpt <= doc && (reinterpret_cast<uintptr_t>(g) & 15u) == 0) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(g + base);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(g + base);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(g + base + 4);
 #pragma unroll
-    for (int j = 0; j < kHistKpt; ++j) atomicAdd(&sh.hist[order_key(v[j]) >> 21], 1u);
+    for (int j = 0; j < 4; ++j) atomicAdd(&sh.hist[order_key(v0[j]) >> 21], 1u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) atomicAdd(&sh.hist[order_key(v1[j]) >> 21], 1u);
   } else {
 #pragma unroll
     for (int j = 0; j < kHistKpt; ++j)
       if (base + j < doc) atomicAdd(&sh.hist[order_key(g[base + j]) >> 21], 1u);
   }
   __syncthreads();
-  if (!sel_publish_and_arrive<kHistThreads>(sh, ws)) return;
-  select_finish<kHistThreads, KPT_FIN>(sh, g, doc, kd, q, out, ws);
+  if (!sel_publish_and_arrive<kHistThreads, false>(sh, ws)) return;
+  SelKeys kp;
+  kp.page[0] = kp.page[1] = kp.page[2] = keys;
+  kp.page_tokens = kFinishBlock;
+  kp.block_tokens = kFinishBlock;
+  select_finish<kHistThreads>(sh, kp, g, doc, kd, ws);
+}
+
+// Where each kept token goes, from T, need and the chunk counts:
+//   document token j (key k_j):  kept iff k_j > T, or k_j == T and fewer
+//     than `need` keys equal to T come before it; its slot is the number of
+//     kept document tokens before it;
+//   question token j >= doc:     always kept, slot kd + (j - doc).
+struct CompactArgs {
+  const float* g;
+  int n, doc, kd, q;
+  const uint32_t* ws;
+  int32_t* idx;
+  const uint8_t* h;   // rows of h (gather_items_kernel)
+  int64_t ld_bytes;   // bytes between rows of h
+  int row_chunks;     // 16-byte pieces per row
+  uint8_t* h_out;     // [kept, row_chunks * 16] contiguous
+  float* g_out;       // or NULL
+  int32_t* pos_out;   // or NULL
+  int tail_items;     // ceil(q / 8)
+};
+
+// Decision for the 64 tokens of chunk c, one per lane of a wave: the token,
+// its score, whether it is kept and its slot.
+struct ChunkLane {
+  int j;
+  float gj;
+  bool kept;
+  int slot;
+};
+
+__device__ __forceinline__ ChunkLane decide_chunk(const CompactArgs& a, int c, int lane) {
+  ChunkLane r;
+  r.j = c * kCompactChunk + lane;
+  const bool in_doc = r.j < a.doc;
+  const bool in_tail = !in_doc && r.j < a.n;
+  r.gj = (r.j < a.n) ? a.g[r.j] : 0.0f;
+  const uint32_t key = order_key(r.gj);
+  const uint32_t T = a.ws[kSelWsT];
+  const uint32_t need = a.ws[kSelWsNeed];
+  uint32_t gt_b = 0, eq_b = 0;
+  if (c * kCompactChunk < a.doc) {
+    gt_b = a.ws[kSelWsChunks + 2 * c];
+    eq_b = a.ws[kSelWsChunks + 2 * c + 1];
+  }
+  const bool gt = in_doc && key > T;
+  const bool eq = in_doc && key == T;
+  const uint64_t bg = __ballot(gt), be = __ballot(eq);
+  const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+  const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+  const uint32_t eq_rank = eq_b + pe;
+  r.slot = in_doc ? (int)(gt_b + pg + min(eq_rank, need)) : a.kd + (r.j - a.doc);
+  // A slot outside the document's range only comes from a workspace that
+  // does not hold this call's counts: nothing is written for it.
+  r.kept = in_tail || ((gt || (eq && eq_rank < need)) && r.slot < a.kd);
+  return r;
+}
+
+// Indices only: one wave per 64-token chunk of [0, n).
+__global__ __launch_bounds__(64) void compact_kernel(CompactArgs a) {
+  const ChunkLane r = decide_chunk(a, blockIdx.x, threadIdx.x);
+  if (r.kept) a.idx[r.slot] = r.j;
+}
+
+// Indices, rows, gate values and positions: one workgroup of 256 threads per
+// item of at most 8 kept rows.  Workgroups [0, tail_items) take 8 question
+// tokens each; the next ones take the items the ranking listed (those past
+// the listed count return at once).  Wave 0 decides the item's chunk, then
+// the four waves copy two rows each, both rows' loads in flight before the
+// stores.
+__global__ __launch_bounds__(256) void gather_items_kernel(CompactArgs a) {
+  __shared__ int32_t s_src[kItemRows], s_slot[kItemRows];
+  __shared__ float s_g[kItemRows];
+  __shared__ int s_cnt;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  if (b < a.tail_items) {
+    if (threadIdx.x < kItemRows) {
+      const int i = b * kItemRows + threadIdx.x;
+      if (i < a.q) {
+        const int j = a.doc + i, slot = a.kd + i;
+        a.idx[slot] = j;
+        s_src[threadIdx.x] = j;
+        s_slot[threadIdx.x] = slot;
+        s_g[threadIdx.x] = a.g[j];
+      }
+      if (threadIdx.x == 0) s_cnt = min(kItemRows, a.q - b * kItemRows);
+    }
+  } else {
+    const int item = b - a.tail_items;
+    if (item >= (int)a.ws[kSelWsItems]) return;
+    const uint32_t code = a.ws[sel_items_word(a.doc) + item];
+    const int c = (int)(code >> 4), part = (int)(code & 15u);
+    if (wave == 0) {
+      const ChunkLane r = decide_chunk(a, c, lane);
+      const uint64_t bk = __ballot(r.kept);
+      const int kr = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u));
+      const int lo = part * kItemRows;
+      if (r.kept && kr >= lo && kr < lo + kItemRows) {
+        a.idx[r.slot] = r.j;
+        s_src[kr - lo] = r.j;
+        s_slot[kr - lo] = r.slot;
+        s_g[kr - lo] = r.gj;
+      }
+      if (lane == 0) s_cnt = max(0, min(kItemRows, __popcll(bk) - lo));
+    }
+  }
+  __syncthreads();
+  const int nk = s_cnt;
+  const int r0 = 2 * wave;
+  const int nr = min(2, nk - r0);
+  if (nr > 0) {
+    for (int c0 = 0; c0 < a.row_chunks; c0 += 4 * kWave) {
+      u32x4 v[2][4];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int cc = c0 + u * kWave + lane;
+          if (rr < nr && cc < a.row_chunks)
+            v[rr][u] = *reinterpret_cast<const u32x4*>(a.h + (int64_t)s_src[r0 + rr] * a.ld_bytes + cc * 16);
+        }
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int cc = c0 + u * kWave + lane;
+          if (rr < nr && cc < a.row_chunks)
+            *reinterpret_cast<u32x4*>(a.h_out + (int64_t)s_slot[r0 + rr] * a.row_chunks * 16 + cc * 16) = v[rr][u];
+        }
+    }
+  }
+  if (threadIdx.x < nk) {
+    if (a.g_out) a.g_out[s_slot[threadIdx.x]] = s_g[threadIdx.x];
+    if (a.pos_out) a.pos_out[s_slot[threadIdx.x]] = s_src[threadIdx.x];
+  }
 }
 
 }  // namespace
@@ -349,7 +498,38 @@ hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len, co
   return hipGetLastError();
 }
 
-int64_t select_mw_workspace_bytes(int64_t) { return kSelWsBytes; }
+int64_t select_mw_workspace_bytes(int64_t n) { return sel_ws_bytes(n); }
+
+hipError_t launch_compact(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, const void* workspace,
+                          const void* h, int64_t ld_h_bytes, int row_bytes, void* h_out, float* g_out,
+                          int32_t* pos_out, hipStream_t stream) {
+  const int64_t kept = k < n ? k : n;
+  CompactArgs a;
+  a.g = g;
+  a.n = (int)n;
+  a.doc = (int)(n - q_len);
+  a.kd = (int)(kept - q_len);
+  a.q = (int)q_len;
+  a.ws = static_cast<const uint32_t*>(workspace);
+  a.idx = idx;
+  a.h = static_cast<const uint8_t*>(h);
+  a.ld_bytes = ld_h_bytes;
+  a.row_chunks = row_bytes / 16;
+  a.h_out = static_cast<uint8_t*>(h_out);
+  a.g_out = g_out;
+  a.pos_out = pos_out;
+  a.tail_items = (int)((q_len + kItemRows - 1) / kItemRows);
+  if (h_out) {
+    const int64_t blocks = a.tail_items + sel_max_items(a.doc);
+    if (!grid_fits(blocks, 256)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gather_items_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else {
+    const int64_t blocks = sel_chunks(n);
+    if (!grid_fits(blocks, kWave)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(kWave), 0, stream, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, void* workspace,
                             bool ws_clean, hipStream_t stream) {
@@ -362,9 +542,9 @@ hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len,
   if (!grid_fits(blocks, kHistThreads)) return hipErrorInvalidConfiguration;
   auto* ws = static_cast<uint32_t*>(workspace);
   if (!ws_clean) hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, stream, ws);
-  hipLaunchKernelGGL(sel_hist_finish_kernel<32>, dim3((unsigned)blocks), dim3(kHistThreads), 0, stream, g, (int)doc,
-                     (int)kd, (int)q_len, idx, ws);
-  return hipGetLastError();
+  hipLaunchKernelGGL(sel_hist_finish_kernel, dim3((unsigned)blocks), dim3(kHistThreads), 0, stream, g, (int)doc,
+                     (int)kd, ws);
+  return launch_compact(g, n, k, q_len, idx, ws, nullptr, 0, 0, nullptr, nullptr, nullptr, stream);
 }
 
 }  // namespace tg

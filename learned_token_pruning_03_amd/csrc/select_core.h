@@ -9,12 +9,24 @@
 // reading): larger g first, ties to the lower index, NaN last, -0 == +0;
 // kept indices ascending with the question tail last.
 //
-// Workspace of the multi-workgroup forms (uint32 words, zero between calls):
+// Workspace of the multi-workgroup forms (uint32 words):
 //   [0, 2048)   counts of the top 11 bits (31..21) of every document key,
 //               added by every workgroup with device atomics;
 //   [2048]      arrival counter: the workgroup that brings it to gridDim.x is
-//               the last one, sees every count and every score, and finishes
-//               the selection alone.  It clears both before it returns.
+//               the last one, sees every count and every score, and ranks
+//               alone.  It clears the counts and the counter (zero between
+//               calls) and writes the rest:
+//   [2049]      T, the key of the kd-th largest document score;
+//   [2050]      need, how many document keys equal to T are kept;
+//   [2051]      the number of copy items (below);
+//   [2112 + 2c] for each 64-token chunk c of the document: the number of its
+//               keys above T, then equal to T, in the chunks before it;
+//   then        copy items, chunk * 16 + part: part p of chunk c stands for
+//               the chunk's kept tokens of rank 8p .. 8p + 7 (at most 8
+//               rows per item, however the kept tokens cluster).
+// The kernels after it read T, need, the chunk counts and the items: one
+// workgroup per chunk (indices only) or per item (indices and rows) places
+// its kept tokens without any global scan.
 #pragma once
 
 #include "tg_internal.h"
@@ -23,9 +35,21 @@ namespace tg {
 
 constexpr int kSelRadixBits = 11;
 constexpr int kSelBins = 1 << kSelRadixBits;
-constexpr int kSelWsCounter = kSelBins;         // word index of the arrival counter
-constexpr int kSelWsWords = kSelBins + 64;      // 8448 bytes: histogram, counter, padding
-constexpr int64_t kSelWsBytes = kSelWsWords * 4;
+constexpr int kSelWsCounter = kSelBins;  // word index of the arrival counter
+constexpr int kSelWsT = kSelBins + 1;
+constexpr int kSelWsNeed = kSelBins + 2;
+constexpr int kSelWsItems = kSelBins + 3;    // number of copy items
+constexpr int kSelWsChunks = kSelBins + 64;  // first chunk count
+constexpr int kCompactChunk = 64;            // tokens per chunk
+constexpr int kItemRows = 8;                 // kept rows per copy item
+
+__host__ __device__ inline int64_t sel_chunks(int64_t n) { return (n + kCompactChunk - 1) / kCompactChunk; }
+// Copy items of a prompt of n tokens, at most: sum over chunks of
+// ceil(kept_c / 8) <= chunks + kept / 8.
+__host__ __device__ inline int64_t sel_max_items(int64_t n) { return sel_chunks(n) + (n + kItemRows - 1) / kItemRows; }
+__host__ __device__ inline int64_t sel_items_word(int64_t n) { return kSelWsChunks + 2 * sel_chunks(n); }
+// Workspace bytes for a prompt of n tokens.
+inline int64_t sel_ws_bytes(int64_t n) { return (sel_items_word(n) + sel_max_items(n)) * (int64_t)sizeof(uint32_t); }
 
 // Unsigned order of the key == rank order of the score: NaN -> 0 (lowest),
 // -0 -> +0, negatives reversed below positives.
@@ -36,18 +60,51 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kSelMaxBlockChunks = 512;  // 64-token chunks per block of keys held in LDS
+
 struct SelFinishShared {
   uint32_t hist[kSelBins];
   uint32_t red[16][2];
   uint32_t bcast[4];
 };
 
+// A block of keys held in LDS, in up to three pages (the gate keeps them in
+// the three stages of its ring).  The 64-token chunk starting at token i of
+// the block sits in page i / page_tokens.  block_tokens and page_tokens are
+// multiples of 64; block_tokens is at most 64 * kSelMaxBlockChunks and
+// 3 * page_tokens.
+struct SelKeys {
+  uint32_t* page[3];
+  int page_tokens;
+  int block_tokens;
+};
+
+// Selects between the three pages with constant indices: an index computed at
+// run time would put the pointer array in scratch memory.
+__device__ __forceinline__ uint32_t* sel_key_ptr(const SelKeys& k, int i) {
+  if (i >= 2 * k.page_tokens) return k.page[2] + (i - 2 * k.page_tokens);
+  if (i >= k.page_tokens) return k.page[1] + (i - k.page_tokens);
+  return k.page[0] + i;
+}
+
+// Inclusive scan over the 64 lanes of a wave on the DPP lane network (row
+// shifts within 16-lane rows, then the row broadcasts of lanes 15 and 31):
+// six moves with no LDS round trip.
 __device__ __forceinline__ uint32_t sel_wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)v, o, kWave);
-    if (lane >= o) v += y;
-  }
+  const int rl = lane & 15;
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  if (rl >= 1) v += t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  if (rl >= 2) v += t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  if (rl >= 4) v += t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  if (rl >= 8) v += t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);  // row_bcast:15
+  if ((lane & 31) >= 16) v += t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);  // row_bcast:31
+  if (lane >= 32) v += t;
   return v;
 }
 
@@ -85,11 +142,45 @@ __device__ __forceinline__ void sel_block_scan2(SelFinishShared& sh, uint32_t a,
   __syncthreads();
 }
 
-// In sh.hist (kSelBins bins, counts of the keys still in play), the bin that
-// holds the need-th largest key and how many keys of that bin are still to
-// take.  Thread t owns kSelBins / THREADS consecutive bins, highest first.
+// Block-wide exclusive scan of three counters with one LDS round trip; also
+// returns the totals.
 template <int THREADS>
-__device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, uint32_t& bin, uint32_t& rest) {
+__device__ __forceinline__ void sel_block_scan3(SelFinishShared& sh, const uint32_t (&v)[3], uint32_t (&ex)[3],
+                                                uint32_t (&tot)[3]) {
+  constexpr int NW = THREADS / kWave;
+  static_assert(NW <= 8, "block too large for the three-counter scan");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t inc[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) inc[c] = sel_wave_incl_scan(v[c], lane);
+  if (lane == 63) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) (&sh.red[0][0])[3 * wave + c] = inc[c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    uint32_t pre = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = (&sh.red[0][0])[3 * w + c];
+      if (w < wave) pre += x;
+      t += x;
+    }
+    ex[c] = pre + inc[c] - v[c];
+    tot[c] = t;
+  }
+  __syncthreads();
+}
+
+// In sh.hist (kSelBins bins, counts of the keys still in play), the bin that
+// holds the need-th largest key, how many keys of that bin are still to take
+// (rest) and how many keys the bin holds (count).  Thread t owns
+// kSelBins / THREADS consecutive bins, highest first.
+template <int THREADS>
+__device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, uint32_t& bin, uint32_t& rest,
+                                            uint32_t& count, uint32_t* total = nullptr) {
   constexpr int PER = kSelBins / THREADS;
   static_assert(PER >= 1 && PER * THREADS == kSelBins, "bins per thread");
   const int top = kSelBins - 1 - (int)threadIdx.x * PER;
@@ -102,9 +193,11 @@ __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, 
   if (threadIdx.x == 0) {  // defaults, overwritten by exactly one thread below
     sh.bcast[0] = 0u;
     sh.bcast[1] = need;
+    sh.bcast[3] = 0u;
   }
   uint32_t above, dummy, tot, tot2;
   sel_block_scan2<THREADS>(sh, sum, 0u, above, dummy, tot, tot2);
+  if (total) *total = tot;
   if (above < need && above + sum >= need) {
     uint32_t cum = above;
 #pragma unroll
@@ -112,6 +205,7 @@ __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, 
       if (cum + loc[i] >= need) {
         sh.bcast[0] = (uint32_t)(top - i);
         sh.bcast[1] = need - cum;
+        sh.bcast[3] = loc[i];
         break;
       }
       cum += loc[i];
@@ -120,25 +214,38 @@ __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, 
   __syncthreads();
   bin = sh.bcast[0];
   rest = sh.bcast[1];
+  count = sh.bcast[3];
   __syncthreads();
 }
 
 // Adds this workgroup's counts (sh.hist) to the workspace histogram, then
 // counts the workgroup in.  Returns true in exactly one workgroup: the last
-// to arrive, which then sees every count and every score written before the
-// arrival of any workgroup.  Every thread of the block must call it.
-template <int THREADS>
+// to arrive.  Every thread of the block must call it.
+//
+// No agent-scope fence on the way: on this multi-XCD part such a fence writes
+// back the whole L2 of the XCD, which costs microseconds per workgroup.
+// Instead everything another workgroup will read is written past the L2
+// (device atomics for the counts, agent-scope atomic stores for scores
+// written in the same kernel), each thread waits until its own writes have
+// completed (vmcnt 0) before the barrier, and only then does one thread
+// count the workgroup in.  When the scores were written by this kernel, the
+// last workgroup then drops its L2's copies (an agent-scope acquire: an
+// invalidate, no write-back) before it reads them.
+// ACQUIRE: the last workgroup reads scores that other workgroups of the same
+// kernel wrote; without it the scores come from an earlier kernel.
+template <int THREADS, bool ACQUIRE>
 __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint32_t* __restrict__ ws) {
   for (int i = threadIdx.x; i < kSelBins; i += THREADS) {
     const uint32_t c = sh.hist[i];
     if (c) atomicAdd(&ws[i], c);
   }
-  __threadfence();  // release: this thread's score stores and count atomics
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vm<0>();
   __syncthreads();
   if (threadIdx.x == 0) sh.bcast[2] = atomicAdd(&ws[kSelWsCounter], 1u) == gridDim.x - 1 ? 1u : 0u;
   __syncthreads();
   const bool last = sh.bcast[2] != 0u;
-  if (last) __threadfence();  // acquire: every other workgroup's stores and counts
+  if (ACQUIRE && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
 
@@ -148,136 +255,227 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 //   - the top digit's bin holding the kd-th largest key, from the histogram
 //     (rebuilt here from the keys if its total is not `doc`);
 //   - bits 20..10, then 9..0, of the keys still in play, counted in LDS: the
-//     kd-th largest key T and `need`, how many keys equal to T are kept;
-//   - one block scan over (count > T, count == T) places every kept index at
-//     its ascending slot, the first `need` keys equal to T by index;
-//   - the question tail [doc, doc + q) goes to slots [kd, kd + q).
+//     kd-th largest key T and `need`, how many keys equal to T are kept.
+//     When the bin a pass settles on is taken whole, every key at or above
+//     that prefix is kept and the remaining passes are skipped;
+//   - block scans give every 64-token chunk its counts before it and list
+//     the copy items.
 // Requires 0 < kd < doc.  Clears the workspace histogram and counter.
-// Each thread holds KPT consecutive keys of a THREADS * KPT chunk; a document
-// of several chunks is re-read once per pass.
-template <int THREADS, int KPT>
-__device__ void select_finish(SelFinishShared& sh, const float* __restrict__ g, int doc, int kd, int q,
-                              int32_t* __restrict__ out, uint32_t* __restrict__ ws) {
+// Thread t owns chunk t of the block held in LDS (its 16 groups of 4 keys
+// rotated by t, so that the 16 lanes of a quarter-wave read 16 different
+// bank groups); a document of several blocks is re-read once per pass.  A
+// single workgroup runs this once, so every phase is a short loop: each
+// thread visits only the keys still in play (a bit mask over its chunk), and
+// every memory access of a phase is issued before the first wait.
+template <int THREADS>
+__device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys& kp, const float* __restrict__ g,
+                                              int doc, int kd, uint32_t* __restrict__ ws) {
+  constexpr int PER = kSelBins / THREADS;
+  constexpr int kMaxIt = kSelMaxBlockChunks * kCompactChunk / (4 * THREADS);  // 16-byte loads per thread per block
+  static_assert(PER * THREADS == kSelBins && kMaxIt >= 1 && THREADS >= kSelMaxBlockChunks, "block shape");
   const int tid = threadIdx.x;
-  constexpr int kChunk = THREADS * KPT;
-  const int nchunks = (doc + kChunk - 1) / kChunk;
+  const int B = kp.block_tokens;
+  const int nblocks = (doc + B - 1) / B;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(g) & 15u) == 0;
-  uint32_t key[KPT];
-
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    const int base = c * kChunk + tid * KPT;
-    if (vec_ok && base + KPT <= doc) {
-#pragma unroll
-      for (int j = 0; j < KPT; j += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(g + base + j);
-        key[j] = order_key(v[0]);
-        key[j + 1] = order_key(v[1]);
-        key[j + 2] = order_key(v[2]);
-        key[j + 3] = order_key(v[3]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) key[j] = (base + j < doc) ? order_key(g[base + j]) : 0u;
-    }
-  };
-  auto nvalid = [&](int c) __attribute__((always_inline)) {
-    const int r = doc - (c * kChunk + tid * KPT);
-    return r <= 0 ? 0 : (r >= KPT ? KPT : r);
+  const bool owner = tid < B / kCompactChunk;  // this thread owns a chunk of every block
+  uint32_t* const mine = sel_key_ptr(kp, owner ? tid * kCompactChunk : 0);
+  auto slot_of = [](uint32_t* chunk, int t, int grp) __attribute__((always_inline)) {
+    return chunk + 4 * ((grp + t) & 15);
   };
 
-  // ---- top digit: the published histogram, moved to LDS; the workspace is
-  // cleared for the next call as it is read.
-  uint32_t part = 0;
-  for (int i = tid; i < kSelBins; i += THREADS) {
-    const uint32_t c = __hip_atomic_load(&ws[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.hist[i] = c;
-    part += c;
-    ws[i] = 0u;
-  }
-  if (tid == 0) ws[kSelWsCounter] = 0u;
-  if (nchunks == 1) load_chunk(0);
-  uint32_t e0, e1, total, t1;
-  sel_block_scan2<THREADS>(sh, part, 0u, e0, e1, total, t1);
-  if (total != (uint32_t)doc) {
-    // Not the histogram of these keys (a workspace that was not left clean):
-    // count the top digit here instead.
-    for (int i = tid; i < kSelBins; i += THREADS) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) load_chunk(c);
-      const int nv = nvalid(c);
+  // Keys of block c into LDS: coalesced 16-byte loads, all in flight before
+  // the barrier that lets the previous block's readers finish, each stored
+  // in its owner's chunk; a partial vector at the document's end (or scores
+  // not 16-byte aligned) goes through a short scalar loop.  Keys past the
+  // document are never read back (every loop below stops at the chunk's
+  // valid count).
+  int cur = -1;
+  auto load_block = [&](int c) __attribute__((always_inline)) {
+    const int base = c * B;
+    f32x4 v[kMaxIt];
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (j < nv) atomicAdd(&sh.hist[key[j] >> 21], 1u);
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int i = 4 * (tid + it * THREADS);
+      if (vec_ok && i < B && base + i + 4 <= doc) v[it] = *reinterpret_cast<const f32x4*>(g + base + i);
     }
     __syncthreads();
-  }
-
-  uint32_t prefix, need;
-  sel_resolve<THREADS>(sh, (uint32_t)kd, prefix, need);
-
-  // ---- bits 20..10, then 9..0, of the keys that share the prefix so far.
+#pragma unroll
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int i = 4 * (tid + it * THREADS);
+      const int o = i / kCompactChunk;
+      if (vec_ok && i < B && base + i + 4 <= doc)
+        *reinterpret_cast<u32x4*>(slot_of(sel_key_ptr(kp, o * kCompactChunk), o, (i % kCompactChunk) / 4)) =
+            u32x4{order_key(v[it][0]), order_key(v[it][1]), order_key(v[it][2]), order_key(v[it][3])};
+    }
 #pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int known = pass == 0 ? 11 : 22;
-    const int w = pass == 0 ? 11 : 10;
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int i = 4 * (tid + it * THREADS);
+      if (i < B && base + i < doc && !(vec_ok && base + i + 4 <= doc)) {
+        const int o = i / kCompactChunk;
+        uint32_t* kq = slot_of(sel_key_ptr(kp, o * kCompactChunk), o, (i % kCompactChunk) / 4);
+#pragma unroll 1
+        for (int e = 0; e < 4 && base + i + e < doc; ++e) kq[e] = order_key(g[base + i + e]);
+      }
+    }
+    __syncthreads();
+    cur = c;
+  };
+  // Valid keys of this thread's chunk in block c.
+  auto nvalid = [&](int c) __attribute__((always_inline)) {
+    const int r = owner ? doc - (c * B + tid * kCompactChunk) : 0;
+    return r <= 0 ? 0 : (r >= kCompactChunk ? kCompactChunk : r);
+  };
+  // All 64 keys of this thread's chunk (16 reads in flight).
+  auto read_chunk = [&](u32x4 (&k)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) k[i] = *reinterpret_cast<const u32x4*>(slot_of(mine, tid, i));
+  };
+  auto key_at = [&](int j) __attribute__((always_inline)) { return slot_of(mine, tid, j >> 2)[j & 3]; };
+
+  // ---- top digit: the published histogram (read past the L2), into LDS,
+  // with the first block's keys in flight at the same time.
+  uint32_t hc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) hc[i] = __hip_atomic_load(&ws[tid + i * THREADS], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  load_block(0);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sh.hist[tid + i * THREADS] = hc[i];
+  __syncthreads();
+
+  // Phases over the blocks of keys, the current block kept in LDS between
+  // phases: 0 counts the top digit again (only if the published counts do
+  // not add up to doc: a workspace that was not left clean), 1 and 2 count
+  // bits 20..10 and 9..0 of the keys that share the prefix found so far,
+  // 3 counts the keys above and equal to T per chunk and lists the items.
+  uint32_t prefix = 0, need = (uint32_t)kd, T = 0;
+  int phase = 1;
+  {
+    uint32_t bin, rest, cnt, total;
+    sel_resolve<THREADS>(sh, need, bin, rest, cnt, &total);
+    if (total != (uint32_t)doc) {
+      phase = 0;
+    } else {
+      prefix = bin;
+      need = rest;
+      if (rest == cnt) {  // the bin is taken whole: keys > T are those with top digit >= prefix
+        T = (prefix << 21) - 1u;
+        need = 0u;
+        phase = 3;
+      }
+    }
+  }
+  uint32_t* items = ws + sel_items_word(doc);
+  uint32_t run_gt = 0, run_eq = 0, run_items = 0;
+#pragma unroll 1
+  for (; phase < 4; ++phase) {
+    const int known = phase == 1 ? 11 : 22;
+    const int w = phase == 1 ? 11 : 10;
     const int shift = 32 - known - w;
     const uint32_t mask = (1u << w) - 1u;
-    for (int i = tid; i < kSelBins; i += THREADS) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) load_chunk(c);
+    if (phase < 3) {
+      for (int i = tid; i < kSelBins; i += THREADS) sh.hist[i] = 0u;
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int c = 0; c < nblocks; ++c) {
+      if (c != cur) load_block(c);
       const int nv = nvalid(c);
+      u32x4 k[16];
+      read_chunk(k);
+      // Keys past the chunk's valid count are masked off at the end, not
+      // tested one by one.
+      const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+      if (phase < 3) {
+        // The keys of the chunk still in play, then one atomic per such key.
+        uint64_t live = 0;
+        const int sh_known = phase == 0 ? 0 : 32 - known;
+        const uint32_t want = phase == 0 ? 0u : prefix;
+        const uint32_t shmask = phase == 0 ? 0u : 0xffffffffu;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t kk = key[j];
-        if (j < nv && (kk >> (32 - known)) == prefix) atomicAdd(&sh.hist[(kk >> shift) & mask], 1u);
-      }
-    }
-    __syncthreads();
-    uint32_t bin, rest;
-    sel_resolve<THREADS>(sh, need, bin, rest);
-    prefix = (prefix << w) | bin;
-    need = rest;
-  }
-  const uint32_t T = prefix;
-
-  // ---- compaction in index order.
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    if (nchunks > 1) load_chunk(c);
-    const int nv = nvalid(c);
-    uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (j < nv) {
-        cgt += key[j] > T;
-        ceq += key[j] == T;
-      }
-    uint32_t egt, eeq, tgt, teq;
-    sel_block_scan2<THREADS>(sh, cgt, ceq, egt, eeq, tgt, teq);
-    uint32_t gt_before = run_gt + egt;
-    uint32_t eq_before = run_eq + eeq;
-    const int base = c * kChunk + tid * KPT;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (j < nv) {
-        const uint32_t kk = key[j];
-        if (kk > T) {
-          const uint32_t slot = gt_before + min(eq_before, need);
-          if (slot < (uint32_t)kd) out[slot] = base + j;
-          ++gt_before;
-        } else if (kk == T) {
-          const uint32_t slot = gt_before + eq_before;
-          if (eq_before < need && slot < (uint32_t)kd) out[slot] = base + j;
-          ++eq_before;
+        for (int j = 0; j < 64; ++j) {
+          const uint32_t kk = k[j >> 2][j & 3];
+          live |= (uint64_t)(((kk >> sh_known) & shmask) == want) << j;
         }
+        live &= valid;
+#pragma unroll 1
+        while (__ballot(live != 0ull) != 0ull) {
+          if (live != 0ull) {
+            const int j = __builtin_ctzll(live);
+            live &= live - 1ull;
+            const uint32_t kk = key_at(j);
+            atomicAdd(&sh.hist[phase == 0 ? kk >> 21 : (kk >> shift) & mask], 1u);
+          }
+        }
+        continue;
+      }
+      // phase 3: counts of this chunk, then block scans in chunk order.
+      uint64_t mgt = 0, meq = 0;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t kk = k[j >> 2][j & 3];
+        mgt |= (uint64_t)(kk > T) << j;
+        meq |= (uint64_t)(kk == T) << j;
+      }
+      const uint32_t cgt = (uint32_t)__popcll(mgt & valid), ceq = (uint32_t)__popcll(meq & valid);
+      uint32_t gt_b, eq_b, tgt, teq, eni, tni, ni;
+      if (need == 0u) {  // keys equal to T are never kept: the items follow from cgt alone
+        ni = nv > 0 ? (cgt + kItemRows - 1) / kItemRows : 0u;
+        const uint32_t v3[3] = {cgt, ceq, ni};
+        uint32_t ex3[3], tot3[3];
+        sel_block_scan3<THREADS>(sh, v3, ex3, tot3);
+        gt_b = run_gt + ex3[0];
+        eq_b = run_eq + ex3[1];
+        eni = ex3[2];
+        tgt = tot3[0];
+        teq = tot3[1];
+        tni = tot3[2];
+      } else {
+        uint32_t egt, eeq;
+        sel_block_scan2<THREADS>(sh, cgt, ceq, egt, eeq, tgt, teq);
+        gt_b = run_gt + egt;
+        eq_b = run_eq + eeq;
+        const uint32_t kept = cgt + (min(eq_b + ceq, need) - min(eq_b, need));
+        ni = nv > 0 ? (kept + kItemRows - 1) / kItemRows : 0u;
+        uint32_t dummy, tdummy;
+        sel_block_scan2<THREADS>(sh, ni, 0u, eni, dummy, tni, tdummy);
+      }
+      if (nv > 0) {
+        const int ch = c * (B / kCompactChunk) + tid;
+        ws[kSelWsChunks + 2 * ch] = gt_b;
+        ws[kSelWsChunks + 2 * ch + 1] = eq_b;
+#pragma unroll 1
+        for (uint32_t r = 0; r < ni; ++r) items[run_items + eni + r] = (uint32_t)ch * 16u + r;
+      }
+      run_gt += tgt;
+      run_eq += teq;
+      run_items += tni;
+    }
+    if (phase < 3) {
+      __syncthreads();
+      uint32_t bin, rest, cnt;
+      sel_resolve<THREADS>(sh, need, bin, rest, cnt);
+      const int bits_left = phase == 0 ? 21 : (phase == 1 ? 10 : 0);
+      prefix = phase == 0 ? bin : (prefix << w) | bin;
+      need = rest;
+      if (phase == 2) {
+        T = prefix;
+      } else if (rest == cnt) {  // the bin is taken whole
+        T = (prefix << bits_left) - 1u;
+        need = 0u;
+        phase = 2;  // next: phase 3
       }
     }
-    run_gt += tgt;
-    run_eq += teq;
   }
-  for (int i = tid; i < q; i += THREADS) out[kd + i] = doc + i;  // protected tail
+  if (tid == 0) {
+    ws[kSelWsT] = T;
+    ws[kSelWsNeed] = need;
+    ws[kSelWsItems] = run_items;
+  }
+  // ---- the counts and the counter are zero again for the next call.
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    __hip_atomic_store(&ws[tid + i * THREADS], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&ws[kSelWsCounter], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace tg

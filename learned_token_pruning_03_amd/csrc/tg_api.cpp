@@ -103,35 +103,64 @@ TG_API tg_status tg_gate_score(tg_dtype dtype, int64_t n, int32_t d, int32_t hid
   return from_hip(launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream), "gate");
 }
 
+static tg_status gate_select_impl(const char* what, tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,
+                                  const void* h, int64_t ld_h, const void* w1, const float* b1, const float* w2,
+                                  float b2, int64_t k, int64_t q_len, float* g, float* s, int32_t* idx, void* h_out,
+                                  float* g_out, int32_t* pos_out, void* workspace, int64_t workspace_bytes,
+                                  hipStream_t stream) {
+  tg_status st = check_gate(what, dtype, n, d, hidden, h, ld_h, w1, w2, g);
+  if (st != TG_OK) return st;
+  if (k < 0) return fail(TG_ERR_INVALID_ARG, "%s: k=%lld < 0", what, (long long)k);
+  const int64_t kept = k < n ? k : n;
+  if (q_len < 0 || q_len > kept)
+    return fail(TG_ERR_INVALID_ARG, "%s: q_len=%lld outside [0, min(k, n)=%lld]", what, (long long)q_len,
+                (long long)kept);
+  if (n == 0) return ok();
+  if (!idx || !workspace) return fail(TG_ERR_INVALID_ARG, "%s: NULL idx or workspace", what);
+  if (!aligned16(workspace)) return fail(TG_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
+  const int64_t need = tg::select_mw_workspace_bytes(n);
+  if (workspace_bytes < need)
+    return fail(TG_ERR_WORKSPACE, "%s: workspace of %lld bytes, %lld needed", what, (long long)workspace_bytes,
+                (long long)need);
+  const bool gather = h_out != nullptr || g_out != nullptr || pos_out != nullptr;
+  if (gather) {
+    if (!h_out) return fail(TG_ERR_INVALID_ARG, "%s: NULL h_out", what);
+    if (!aligned16(h_out)) return fail(TG_ERR_INVALID_ARG, "%s: h_out must be 16-byte aligned", what);
+  }
+  const int64_t doc = n - q_len, kd = kept - q_len;
+  hipError_t e;
+  if (dtype == TG_BF16 && kd > 0 && kd < doc) {
+    e = tg::launch_gate_select_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, k, q_len, idx, workspace, h_out,
+                                    g_out, pos_out, stream);
+  } else {
+    // fp32, or a budget with nothing to rank: the gate, then the selection
+    // kernels (the one-workgroup kernel writes the identity or the tail
+    // directly when kd says so), then the gather.
+    e = launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
+    if (e == hipSuccess) e = tg::launch_select_mw(g, n, k, q_len, idx, workspace, true, stream);
+    if (e == hipSuccess && gather)
+      e = tg::launch_gather(elem_size(dtype), n, kept, d, idx, h, ld_h, g_out ? g : nullptr, h_out, g_out, pos_out,
+                            nullptr, nullptr, 1, kept, stream);
+  }
+  return from_hip(e, what);
+}
+
 TG_API tg_status tg_gate_select(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden, const void* h, int64_t ld_h,
                                 const void* w1, const float* b1, const float* w2, float b2, int64_t k,
                                 int64_t q_len, float* g, float* s, int32_t* idx, void* workspace,
                                 int64_t workspace_bytes, hipStream_t stream) {
-  tg_status st = check_gate("gate_select", dtype, n, d, hidden, h, ld_h, w1, w2, g);
-  if (st != TG_OK) return st;
-  if (k < 0) return fail(TG_ERR_INVALID_ARG, "gate_select: k=%lld < 0", (long long)k);
-  const int64_t kept = k < n ? k : n;
-  if (q_len < 0 || q_len > kept)
-    return fail(TG_ERR_INVALID_ARG, "gate_select: q_len=%lld outside [0, min(k, n)=%lld]", (long long)q_len,
-                (long long)kept);
-  if (n == 0) return ok();
-  if (!idx || !workspace) return fail(TG_ERR_INVALID_ARG, "gate_select: NULL idx or workspace");
-  if (!aligned16(workspace)) return fail(TG_ERR_INVALID_ARG, "gate_select: workspace must be 16-byte aligned");
-  const int64_t need = tg::select_mw_workspace_bytes(n);
-  if (workspace_bytes < need)
-    return fail(TG_ERR_WORKSPACE, "gate_select: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
-                (long long)need);
-  const int64_t doc = n - q_len, kd = kept - q_len;
-  hipError_t e;
-  if (dtype == TG_BF16 && kd > 0 && kd < doc) {
-    e = tg::launch_gate_select_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, k, q_len, idx, workspace, stream);
-  } else {
-    // fp32, or a budget with nothing to rank: the gate, then the selection
-    // kernel (which writes the identity or the tail directly when kd says so).
-    e = launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
-    if (e == hipSuccess) e = tg::launch_select_mw(g, n, k, q_len, idx, workspace, true, stream);
-  }
-  return from_hip(e, "gate_select");
+  return gate_select_impl("gate_select", dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, k, q_len, g, s, idx, nullptr,
+                          nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+TG_API tg_status tg_gate_select_gather(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden, const void* h,
+                                       int64_t ld_h, const void* w1, const float* b1, const float* w2, float b2,
+                                       int64_t k, int64_t q_len, float* g, float* s, int32_t* idx, void* h_out,
+                                       float* g_out, int32_t* pos_out, void* workspace, int64_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (!h_out) return fail(TG_ERR_INVALID_ARG, "gate_select_gather: NULL h_out");
+  return gate_select_impl("gate_select_gather", dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, k, q_len, g, s, idx,
+                          h_out, g_out, pos_out, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -89,12 +89,14 @@ inline bool grid_fits(int64_t blocks_x, int threads, int64_t y = 1, int64_t z = 
 hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h,
                             const void* w1, const float* b1, const float* w2, float b2,
                             float* g, float* s, hipStream_t stream);
-// Gate MLP whose last workgroup also selects the top-K tokens of the scores it
-// wrote (bf16 only; workspace zero on entry, zero again on exit).  Requires
-// 0 < kd = min(k, n) - q_len < n - q_len.
+// Gate MLP whose last workgroup also ranks the scores it wrote (bf16 only;
+// select workspace zero on entry, zero again on exit), then the compaction
+// kernel: idx, and with h_out the kept rows, gate values and positions.
+// Requires 0 < kd = min(k, n) - q_len < n - q_len.
 hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
                                    const float* b1, const float* w2, float b2, float* g, float* s, int64_t k,
-                                   int64_t q_len, int32_t* idx, void* workspace, hipStream_t stream);
+                                   int64_t q_len, int32_t* idx, void* workspace, void* h_out, float* g_out,
+                                   int32_t* pos_out, hipStream_t stream);
 hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t ld_h,
                            const float* w1, const float* b1, const float* w2, float b2,
                            float* g, float* s, hipStream_t stream);
@@ -105,6 +107,12 @@ hipError_t launch_gate_f32(int64_t n, int d, int hidden, const float* h, int64_t
 int64_t select_mw_workspace_bytes(int64_t n);
 hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, void* workspace,
                             bool ws_clean, hipStream_t stream);
+// Compaction after a multi-workgroup ranking (T, need and the chunk counts in
+// the workspace): idx, and with h_out != NULL also the kept rows of h
+// (row_bytes each, ld_h_bytes apart), their gate values and positions.
+hipError_t launch_compact(const float* g, int64_t n, int64_t k, int64_t q_len, int32_t* idx, const void* workspace,
+                          const void* h, int64_t ld_h_bytes, int row_bytes, void* h_out, float* g_out,
+                          int32_t* pos_out, hipStream_t stream);
 hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len,
                          const int32_t* cu_seqlens, const int32_t* q_lens, int batch,
                          int64_t max_seqlen, int32_t* idx, int32_t* cu_kept,

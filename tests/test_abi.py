@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
-    for name in ("tg_gate_score", "tg_gate_select", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
+    for name in ("tg_gate_score", "tg_gate_select", "tg_gate_select_gather", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
                  "tg_select_topk_ws", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
@@ -220,8 +220,10 @@ def test_grids_beyond_one_dispatch_are_refused_before_any_hip_call(lib):
 
 def test_select_ws_validation_without_a_gpu(lib):
     ws = lib.tg_select_topk_workspace_size(32768)
-    assert ws >= (2048 + 1) * 4  # one 11-bit histogram and an arrival counter
-    assert lib.tg_select_topk_workspace_size(1 << 30) == ws  # the same for every prompt length
+    # an 11-bit histogram, an arrival counter, T, need and the item count; two counts per 64-token
+    # chunk; then up to one copy item per chunk plus one per 8 tokens
+    assert ws == (2048 + 64) * 4 + 8 * (32768 // 64) + 4 * (32768 // 64 + 32768 // 8)
+    assert lib.tg_select_topk_workspace_size(100) == (2048 + 64) * 4 + 8 * 2 + 4 * (2 + 13)
     assert lib.tg_select_topk_workspace_size(-1) == -1
     ok = tg.TG_ERR_INVALID_ARG
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == tg.TG_ERR_WORKSPACE
@@ -252,6 +254,14 @@ def test_gate_select_validation_without_a_gpu(lib):
     assert call(d=100) == U
     assert call(h=FAKE + 2) == E
     assert call(n=0, h=None, w1=None, w2=None, g=None, idx=None, wsp=None, k=0, q=0) == tg.TG_OK  # empty: no-op
+    # the gathering form also needs an aligned h_out
+    gsg = lib.tg_gate_select_gather
+    assert gsg(tg.TG_BF16, 32768, 2048, 256, FAKE, 2048, FAKE, None, FAKE, 0.0, 4096, 64, FAKE, None, FAKE, None,
+               None, None, FAKE, ws, None) == E
+    assert gsg(tg.TG_BF16, 32768, 2048, 256, FAKE, 2048, FAKE, None, FAKE, 0.0, 4096, 64, FAKE, None, FAKE, FAKE + 4,
+               None, None, FAKE, ws, None) == E
+    assert gsg(tg.TG_BF16, 32768, 2048, 256, FAKE, 2048, FAKE, None, FAKE, 0.0, 4096, 64, FAKE, None, FAKE, FAKE,
+               None, None, FAKE, ws - 4, None) == W
 
 
 def test_binding_rejects_mismatched_buffers_before_any_call():

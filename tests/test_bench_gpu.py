@@ -38,14 +38,14 @@ def test_bench_prints_one_json_line_with_the_roofline(gpu_lib):
     assert abs(roof["achieved"] - roof["flops_per_launch"] / (roof["avg_launch_us"] * 1e-6) / 1e12) < 0.5
     assert roof["launches_timed"] == 3
     assert out["cpu_baseline"] is None  # switched off for this run
-    for stage in ("gate_select", "gather", "rope_kv", "attn"):  # the step's own stages, in path order
+    for stage in ("prune", "rope_kv", "attn"):  # the step's own stages, in path order
         assert out["stages"][stage]["median_us"] > 0
-    for stage in ("gate_select", "gate", "select", "gather", "rope_kv", "attn"):
+    for stage in ("prune", "gate", "gate_select", "select", "gather", "rope_kv", "attn"):
         assert out["stages"][stage]["cold_us"] > 0
         assert out["stages"][stage]["us_back_to_back"] > 0
     assert out["stages"]["gather"]["back_to_back_cache"] == "cold"
-    assert out["prune_entry"] == "tg_gate_select"
+    assert out["prune_entry"] == "tg_gate_select_gather"
     for key in ("gather_pct_hbm_peak", "gate_pct_hbm_peak", "rope_kv_pct_hbm_peak"):
         assert 0 < out[key] < 100, key
-    assert out["pruning"]["gather_us"] > 0 and out["pruning"]["gate_select_us"] > 0
+    assert out["pruning"]["select_plus_gather_us"] > 0 and out["pruning"]["prune_us"] > 0
     assert roof["avg_launch_us_back_to_back"] > 0 and 0 < roof["frac_back_to_back"] < 1

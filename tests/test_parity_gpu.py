@@ -193,16 +193,31 @@ def test_select_varlen_ragged_batch(gpu_lib):
 
 # ----------------------------------------------------------------------------- gate + select in one call
 def _gate_select_case(tg, h, w1, b1, w2, b2, k, q, ws=None):
-    """tg_gate_select against the plain gate on the same input (the same g, bit
-    for bit) and the oracle's selection on the g it wrote (bit-exact)."""
+    """tg_gate_select and tg_gate_select_gather against the plain gate on the
+    same input (the same g, bit for bit), the oracle's selection on the g they
+    wrote (bit-exact) and the oracle's gather of those rows (bit-exact)."""
     hd, w1d, b1d, w2d = h.to(DEV), w1.to(DEV), b1.to(DEV), w2.to(DEV)
     g, idx = tg.tg_gate_select(hd, w1d, b1d, w2d, b2, k, q, workspace=ws)
+    g2, idx2, hk, gk, pos = tg.tg_gate_select_gather(hd, w1d, b1d, w2d, b2, k, q, workspace=ws)
     g_plain = tg.tg_gate_score(hd, w1d, b1d, w2d, b2)
     torch.cuda.synchronize()
     g_cpu = g.cpu().numpy()
     np.testing.assert_array_equal(g_cpu.view(np.uint32), g_plain.cpu().numpy().view(np.uint32))
-    np.testing.assert_array_equal(idx.cpu().numpy().astype(np.int64), ref_select(g_cpu, k, q))
+    np.testing.assert_array_equal(g2.cpu().numpy().view(np.uint32), g_cpu.view(np.uint32))
+    want = ref_select(g_cpu, k, q)
+    np.testing.assert_array_equal(idx.cpu().numpy().astype(np.int64), want)
+    np.testing.assert_array_equal(idx2.cpu().numpy().astype(np.int64), want)
+    bits = h.view(torch.int16).numpy() if h.dtype == torch.bfloat16 else h.view(torch.int32).numpy()
+    wh, wg, wp = ref_gather(bits, g_cpu, want)
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16 if h.dtype == torch.bfloat16 else torch.int32).numpy(), wh)
+    np.testing.assert_array_equal(gk.cpu().numpy().view(np.uint32), np.asarray(wg, dtype=np.float32).view(np.uint32))
+    np.testing.assert_array_equal(pos.cpu().numpy(), wp)
     return g_cpu
+
+
+def _counts_clean(ws):
+    """The histogram and the arrival counter (first 2049 words) are zero."""
+    return int(ws[:2049 * 4].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("n,d,hidden,k,q,planted", [
@@ -238,7 +253,7 @@ def test_gate_select_ties(gpu_lib, b2, dup):
 
 def test_gate_select_reuses_its_workspace(gpu_lib):
     """One workspace across calls of different lengths and budgets: each call
-    leaves it zero-filled, as the next one needs."""
+    leaves its counts and arrival counter zero, as the next one needs."""
     _say("gate_select workspace reuse")
     ws = gpu_lib.select_workspace(50000, DEV)
     for n, d, k, q, seed in [(40000, 256, 5000, 64, 1), (1000, 128, 300, 8, 2), (32768, 2048, 4096, 64, 3),
@@ -247,7 +262,7 @@ def test_gate_select_reuses_its_workspace(gpu_lib):
         w1, b1, w2, _ = W.gate_weights(d, 256, torch.bfloat16, seed)
         _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
         torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+        assert _counts_clean(ws), "counts and counter not left zero"
 
 
 def test_gate_select_recounts_a_histogram_that_does_not_add_up(gpu_lib):
@@ -262,7 +277,7 @@ def test_gate_select_recounts_a_histogram_that_does_not_add_up(gpu_lib):
     w1, b1, w2, _ = W.gate_weights(d, 256, torch.bfloat16, 51)
     _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
     torch.cuda.synchronize()
-    assert int(ws.count_nonzero()) == 0
+    assert _counts_clean(ws)
 
 
 def test_gate_select_fp32_tiny(gpu_lib):
