@@ -22,7 +22,8 @@
  * ---------------------------------------
  *  - Every pointer is a DEVICE pointer unless its comment says otherwise.  The
  *    caller allocates and owns every buffer; the library never allocates and
- *    keeps no state besides a thread-local error message.
+ *    keeps no state besides a thread-local error message (and the static
+ *    scratch array of tg_decode_attn_noalloc).
  *  - Every call only enqueues work on `stream` (0 = the null stream) and returns
  *    without synchronising.  Calls are thread-safe; calls on different streams
  *    may run concurrently if their output buffers do not overlap.
@@ -381,6 +382,28 @@ TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32
                                 const void* v_cache, const float* g, const float* head_gain,
                                 void* o, float* lse, void* workspace, int64_t workspace_bytes,
                                 hipStream_t stream);
+
+/* Decode attention for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation, arguments and errors as tg_decode_attn, with no workspace
+ * argument: the split-K partial results go to a file-scope device array of
+ * tg_decode_attn_noalloc_max_bytes() bytes (16 MiB), which each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing;
+ * its first call on a device looks up that device's copy of the array (with
+ * the device current: `stream` must belong to the current device).
+ *  - A request whose workspace (tg_decode_attn_workspace_size) exceeds the
+ *    array returns TG_ERR_WORKSPACE before any HIP call.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero): calls that
+ *    overlap on one GPU (different streams, or threads) race.  Order them.
+ * The array is global state of the library, the one exception to the
+ * convention above. */
+TG_API int64_t tg_decode_attn_noalloc_max_bytes(void);
+TG_API tg_status tg_decode_attn_noalloc(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                        int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh,
+                                        float scale, const void* q, const void* k_cache,
+                                        const void* v_cache, const float* g, const float* head_gain,
+                                        void* o, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Upper-layer dense work on the kept tokens.  [aitu] section 3: every layer

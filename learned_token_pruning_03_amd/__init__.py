@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     status_string,
     tg_check_positions,
     tg_decode_attn,
+    tg_decode_attn_noalloc,
     tg_decode_attn_workspace_size,
     select_workspace,
     tg_gate_score,

@@ -65,6 +65,9 @@ SIGNATURES = {
                      _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_check_positions": ([_c_vp, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "tg_decode_attn_workspace_size": ([_c_i32, _c_i64, _c_i32, _c_i32, _c_i32], _c_i64),
+    "tg_decode_attn_noalloc_max_bytes": ([], _c_i64),
+    "tg_decode_attn_noalloc": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
+                                _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_decode_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp], ctypes.c_int),
 }
@@ -509,6 +512,37 @@ def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                               _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(g), _ptr(head_gain), _ptr(o), _ptr(lse),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o
+
+
+def tg_decode_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, g: Optional[torch.Tensor],
+                           cu_seqlens: torch.Tensor, max_seqlen: int, o: torch.Tensor,
+                           lse: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                           head_gain: Optional[torch.Tensor] = None):
+    """tg_decode_attn with the library's static scratch instead of a workspace:
+    the library allocates nothing (and neither does this wrapper: o, and lse
+    if wanted, are the caller's).  Returns o."""
+    lib = load_library()
+    _need(q.dim() == 3, "q must be [B, hq, dh]")
+    batch, hq, dh = q.shape
+    hkv = k_cache.shape[1] if k_cache.dim() == 3 else -1
+    _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
+    _need(cu_seqlens.numel() == batch + 1, "cu_seqlens is int32 [B + 1]")
+    _need(q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous(), "q and caches contiguous")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and the caches share a dtype")
+    _need(k_cache.dim() == 3 and k_cache.shape[2] == dh and tuple(v_cache.shape) == tuple(k_cache.shape),
+          "k_cache and v_cache must be [total, hkv, dh]")
+    _vec(g, k_cache.shape[0], torch.float32, "g")
+    _vec(head_gain, hq, torch.float32, "head_gain")
+    _like(o, q.shape, q.dtype, "o")
+    if lse is not None:
+        _like(lse, (batch, hq), torch.float32, "lse")
+    if scale is None:
+        scale = dh ** -0.5
+    _check("tg_decode_attn_noalloc",
+           lib.tg_decode_attn_noalloc(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), hq, hkv, dh,
+                                      float(scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(g), _ptr(head_gain),
+                                      _ptr(o), _ptr(lse), _stream(q)))
+    return o
 
 
 def tg_linear(x: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None,

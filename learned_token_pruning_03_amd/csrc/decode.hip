@@ -24,6 +24,8 @@
 //    the partial results of the blocks and writes o and lse.
 #include <cmath>
 
+#include <mutex>
+
 #include "tg_internal.h"
 
 namespace tg {
@@ -388,6 +390,37 @@ hipError_t launch_dh(const DecArgs& a, int batch, int64_t max_seqlen, hipStream_
 }
 
 }  // namespace
+
+// ---- workspace for the entry point that allocates nothing ----------------
+// A file-scope device array (each device holds its own copy, at its own
+// address, until the process ends).  Host code never passes `scratch`
+// itself to a kernel: on the host that name is a stand-in, not a device
+// address.  The address of each device's copy is looked up once, with that
+// device current, and kept.
+static __device__ __align__(256) uint8_t scratch[kDecodeStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, int64_t max_seqlen, int hq,
                          int hkv, int dh, float scale, const void* q, const void* k, const void* v,

@@ -393,6 +393,50 @@ TG_API int64_t tg_decode_attn_workspace_size(int32_t batch, int64_t max_seqlen, 
   return decode_ws_bytes(batch, max_seqlen, hq, hkv, dh);
 }
 
+static tg_status check_decode(const char* what, tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                              int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale, const void* q,
+                              const void* k_cache, const void* v_cache, void* o) {
+  if (!valid_dtype(dtype)) return fail(TG_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
+  if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32)
+    return fail(TG_ERR_INVALID_ARG, "%s: batch or max_seqlen out of range", what);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(TG_ERR_INVALID_ARG, "%s: hq=%d must be a positive multiple of hkv=%d", what, hq, hkv);
+  const int group = hq / hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(TG_ERR_UNSUPPORTED, "%s: hq/hkv=%d must be 1, 2, 4 or 8", what, group);
+  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "%s: dh=%d must be 64 or 128", what, dh);
+  if (!(scale > 0.0f) || scale != scale) return fail(TG_ERR_INVALID_ARG, "%s: scale must be > 0", what);
+  if (batch == 0) return TG_OK;
+  if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "%s: batch above %d", what, kMaxGridYZ);
+  if (!cu_seqlens || !q || !k_cache || !v_cache || !o) return fail(TG_ERR_INVALID_ARG, "%s: NULL pointer argument", what);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(TG_ERR_INVALID_ARG, "%s: q, k_cache and v_cache must be 16-byte aligned", what);
+  return TG_OK;
+}
+
+TG_API int64_t tg_decode_attn_noalloc_max_bytes(void) { return tg::kDecodeStaticScratchBytes; }
+
+TG_API tg_status tg_decode_attn_noalloc(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
+                                        int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
+                                        const void* q, const void* k_cache, const void* v_cache, const float* g,
+                                        const float* head_gain, void* o, float* lse, hipStream_t stream) {
+  tg_status st = check_decode("decode_noalloc", dtype, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k_cache,
+                              v_cache, o);
+  if (st != TG_OK) return st;
+  if (batch == 0) return ok();
+  const int64_t need = decode_ws_bytes(batch, max_seqlen, hq, hkv, dh);
+  if (need > tg::kDecodeStaticScratchBytes)
+    return fail(TG_ERR_WORKSPACE, "decode_noalloc: needs %lld bytes of scratch, the static scratch holds %lld; "
+                "use tg_decode_attn with a caller workspace", (long long)need,
+                (long long)tg::kDecodeStaticScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = tg::decode_static_scratch(&ws);
+  if (e != hipSuccess) return from_hip(e, "decode_noalloc: looking up the static scratch");
+  return from_hip(tg::launch_decode(elem_size(dtype), cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k_cache,
+                                    v_cache, g, head_gain, o, lse, static_cast<float*>(ws), stream),
+                  "decode_noalloc");
+}
+
 TG_API tg_status tg_decode_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
                                 int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
                                 const void* q, const void* k_cache, const void* v_cache, const float* g,

@@ -145,6 +145,11 @@ hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
 // Decode attention: keys per split-K block, and the launch of the split and
 // combine kernels (workspace: batch * hq * nsplit * (dh + 2) floats).
 int decode_split_keys(int64_t batch, int hkv, int64_t max_seqlen);
+// The decode workspace of the entry point that allocates nothing: a
+// file-scope device array of this many bytes in decode.hip, and the device
+// address of the current device's copy (looked up once per device).
+constexpr int64_t kDecodeStaticScratchBytes = int64_t(16) << 20;
+hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_decode(int elem_bytes, const int32_t* cu_seqlens, int batch, int64_t max_seqlen, int hq,
                          int hkv, int dh, float scale, const void* q, const void* k, const void* v,
                          const float* g, const float* head_gain, void* o, float* lse, float* workspace,

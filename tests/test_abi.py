@@ -305,3 +305,17 @@ def test_binding_rejects_mismatched_buffers_before_any_call():
         with pytest.raises(ValueError):
             case()
             pytest.fail(f"case {i} was not refused")
+
+
+def test_noalloc_decode_refuses_oversized_requests_without_a_gpu(lib):
+    """The static-scratch decode checks its scratch need on the host, before any
+    HIP call, and names the limit."""
+    assert lib.tg_decode_attn_noalloc_max_bytes() == 16 << 20
+    st = lib.tg_decode_attn_noalloc(tg.TG_BF16, FAKE, 64, 1 << 20, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None,
+                                    FAKE, None, None)
+    assert st == tg.TG_ERR_WORKSPACE
+    assert "static scratch" in _err(lib)
+    assert lib.tg_decode_attn_noalloc(tg.TG_BF16, FAKE, 0, 16, 16, 8, 128, 0.1, None, None, None, None, None, None,
+                                      None, None) == tg.TG_OK  # empty batch: no-op
+    assert lib.tg_decode_attn_noalloc(tg.TG_BF16, FAKE, 2, 16, 16, 8, 100, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
+                                      None, None) == tg.TG_ERR_UNSUPPORTED  # dh
