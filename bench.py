@@ -280,16 +280,22 @@ def time_stages(path, reps):
     return {n: statistics.median(v) for n, v in samples.items()}, {n: sum(v) / len(v) for n, v in samples.items()}
 
 
-FLUSH_BYTES = 1 << 30  # written between cold launches: 4x the 256 MB last-level cache
+FLUSH_BYTES = 1 << 30  # read between cold launches: 4x the 256 MB last-level cache
+
+
+def flush_caches(flush):
+    """Reads the whole flush buffer (a reduction, no writes: writing it would
+    leave dirty lines whose write-back the next kernel would pay for)."""
+    flush.amax()
 
 
 def cold_stages(path, reps):
-    """Per-launch event pairs of each stage after 1 GiB has been written to a
+    """Per-launch event pairs of each stage after 1 GiB has been read from a
     scratch buffer (outside the pair), so that no input is served by the L2s or
     the 256 MB last-level cache.  The pair also holds the launch's dispatch
     latency (a few us), so these figures are upper bounds."""
     import torch
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=path.dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=path.dev)
     fns = path_stage_fns(path) + reference_fns(path)
     seen = set()
     out = {}
@@ -300,7 +306,7 @@ def cold_stages(path, reps):
         seen.add(n)
         ts = []
         for r in range(reps):
-            flush.fill_(float(r))
+            flush_caches(flush)
             ev[0].record()
             fn()
             ev[1].record()
@@ -334,10 +340,10 @@ def back_to_back(path, reps=24):
     sh, dev, tg = path.sh, path.dev, path.tg
     kept = min(sh.k, sh.n)
     out = {}
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def timed(name, launches):
-        flush.fill_(1.0)
+        flush_caches(flush)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         for fn in launches:

@@ -297,7 +297,12 @@ TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t 
  *           (every key weighs 1: plain causal GQA attention, the form of the
  *           full-context layers at or below the selection layer).
  *   pos     [n_kept] int32 original positions, strictly increasing (the
- *           order select + gather produce).  Precondition, not checked.
+ *           order select + gather produce).  Precondition, not checked:
+ *           both dtypes apply the causal mask by kept index (key j visible
+ *           to query i iff j <= i), which is the mask above whenever the
+ *           positions strictly increase; the values of pos are not read
+ *           (tg_check_positions verifies the precondition on the device).
+ *           Must be non-NULL.
  *   o       [n_kept, hq, dh] output, dtype.
  *   lse     [hq, n_kept] fp32 output (natural log), or NULL.
  * ------------------------------------------------------------------------- */
@@ -457,7 +462,8 @@ TG_API tg_status tg_qkv_proj(tg_dtype dtype, int64_t m, int32_t hq, int32_t hkv,
 
 /* Check of the position precondition of the attention entry points (the
  * pages' causal mask is on original positions; with strictly increasing
- * positions it equals the mask on kept indices, which the bf16 kernels use).
+ * positions it equals the mask on kept indices, which the attention kernels
+ * of both dtypes use).
  * Writes to *first_bad (device int32) the smallest row i that breaks the
  * order -- pos[i] < 0, or pos[i] <= pos[i-1] with row i-1 in the same
  * sequence -- or `total` when every row is in order.  cu_seqlens [batch+1]

@@ -549,21 +549,21 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: one thread per query, keys streamed through LDS in tiles of 64,
-// natural-base online softmax with the ln g bias.
+// natural-base online softmax with the ln g bias.  Causal by kept index, as the
+// bf16 kernels: key j is visible to query i iff j <= i, which is the mask on
+// original positions whenever they strictly increase.
 template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ q,
                                                       const float* __restrict__ k,
                                                       const float* __restrict__ v,
                                                       const float* __restrict__ g,
                                                       const float* __restrict__ head_gain,
-                                                      const int32_t* __restrict__ pos,
                                                       float* __restrict__ o, float* __restrict__ lse,
                                                       const int32_t* __restrict__ cu, int total, int hq,
                                                       int hkv, float scale) {
   __shared__ float ks[64][DH];
   __shared__ float vs[64][DH];
   __shared__ float bs[64];
-  __shared__ int ps[64];
   const int lane = threadIdx.x;
   const int head = blockIdx.y;
   const int kvh = head / (hq / hkv);
@@ -582,7 +582,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   const float* qp = q + ((s0 + qrow) * hq + head) * DH;
 #pragma unroll
   for (int d = 0; d < DH; ++d) qv[d] = qp[d];
-  const int pos_i = pos[s0 + qrow];
   float m = -INFINITY, l = 0.0f;
   float ov[DH];
 #pragma unroll
@@ -599,12 +598,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     {
       const int j = k0 + lane;
       bs[lane] = j < L ? (g ? logf(fmaxf(g[s0 + j], kFltMin)) * gain : 0.0f) : -INFINITY;
-      ps[lane] = j < L ? pos[s0 + j] : 0x7fffffff;
     }
     __syncthreads();
     const int nk = min(64, kend - k0);
     for (int jj = 0; jj < nk; ++jj) {
-      if (ps[jj] > pos_i) continue;
+      if (k0 + jj > qi) break;
       float sdot = 0.0f;
 #pragma unroll
       for (int d = 0; d < DH; ++d) sdot = fmaf(qv[d], ks[jj][d], sdot);
@@ -673,15 +671,15 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
 
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch, int64_t max_seqlen,
                            int hq, int hkv, int dh, float scale, const float* q, const float* k,
-                           const float* v, const float* g, const float* head_gain, const int32_t* pos,
-                           float* o, float* lse, hipStream_t stream) {
+                           const float* v, const float* g, const float* head_gain, float* o,
+                           float* lse, hipStream_t stream) {
   if (!grid_fits((max_seqlen + 63) / 64, 64, hq, cu_seqlens ? batch : 1)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((max_seqlen + 63) / 64), (unsigned)hq, cu_seqlens ? (unsigned)batch : 1u);
   if (dh == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos, o,
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, o,
                        lse, cu_seqlens, (int)total, hq, hkv, scale);
   else
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos, o,
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, o,
                        lse, cu_seqlens, (int)total, hq, hkv, scale);
   return hipGetLastError();
 }

@@ -320,7 +320,7 @@ static hipError_t dispatch_attn(tg_dtype dtype, int64_t total, const int32_t* cu
                                 pos, o, lse, stream);
   return tg::launch_attn_f32(total, cu, batch, max_seqlen, hq, hkv, dh, scale,
                              static_cast<const float*>(q), static_cast<const float*>(k),
-                             static_cast<const float*>(v), g, head_gain, pos, static_cast<float*>(o),
+                             static_cast<const float*>(v), g, head_gain, static_cast<float*>(o),
                              lse, stream);
 }
 

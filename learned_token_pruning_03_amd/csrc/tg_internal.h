@@ -139,7 +139,7 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
                            int64_t max_seqlen, int hq, int hkv, int dh, float scale,
                            const float* q, const float* k, const float* v, const float* g,
-                           const float* head_gain, const int32_t* pos, float* o, float* lse,
+                           const float* head_gain, float* o, float* lse,
                            hipStream_t stream);
 
 // Decode attention: keys per split-K block, and the launch of the split and

@@ -603,6 +603,27 @@ def test_attn_first_query_is_its_own_value(gpu_lib):
     np.testing.assert_array_equal(o[0], v[0, [0, 0, 1, 1]].double().numpy())
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+def test_attn_masks_by_kept_index_not_position_values(gpu_lib, dtype, tol):
+    """Positions that break the strictly increasing precondition (repeats,
+    descents, -1 as gather writes for an out-of-range index) do not change the
+    output: both dtypes mask by kept index, which the oracle computes with
+    positions 0..n-1.  The outputs are bit-identical to a call with those."""
+    n = 200
+    q, k, v, g, _ = _attn_inputs(n, 4, 2, 64, dtype, 11, "uniform")
+    rng = np.random.default_rng(11)
+    bad = rng.integers(-1, 50, n).astype(np.int32)
+    bad[10:20] = 7
+    bad[0] = -1
+    o_bad, lse_bad = _run_attn(gpu_lib, q, k, v, g, torch.from_numpy(bad))
+    o_idx, lse_idx = _run_attn(gpu_lib, q, k, v, g, torch.arange(n, dtype=torch.int32))
+    np.testing.assert_array_equal(o_bad, o_idx)
+    np.testing.assert_array_equal(lse_bad, lse_idx)
+    wo, wl = ref_attn(q, k, v, g, np.arange(n))
+    assert np.max(np.abs(o_bad - wo)) <= tol
+    assert np.max(np.abs(lse_bad - wl)) <= 1e-3
+
+
 # ----------------------------------------------------------------------------- end to end
 def test_end_to_end_qwen_32k(gpu_lib):
     """The full path at the 32k workload: each stage checked against the oracle
