@@ -66,9 +66,10 @@ def _file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-# The multi-workgroup select costs a fixed ~27 us (six short kernels) where the
-# one-workgroup kernel grows with the prompt: 21 us at 16k tokens, 32 us at
-# 32k, 114 us at 128k (events, one MI355X).
+# The stand-alone multi-workgroup select (a clearing kernel, a histogram kernel
+# whose last workgroup ranks, a compaction) costs ~27-34 us per call at any
+# length, where the one-workgroup kernel grows with the prompt: 21 us at 16k
+# tokens, 32 us at 32k, 114 us at 128k (events, one MI355X).
 SELECT_WS_FROM = 24576
 
 
@@ -718,6 +719,43 @@ def _pmc_per_dispatch(folder, counter, match):
     return sum(per.values()) / len(per), len(per)
 
 
+def _pmc_all_kernels(folder, counter):
+    """{kernel name: (mean of `counter` per dispatch, dispatches)} over every
+    kernel in rocprofv3 csv counter-collection output."""
+    import csv
+    import glob
+    per = {}
+    for fn in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r.get("Kernel_Name", "").replace("(anonymous namespace)::", "").replace("void ", "")
+                name = name.split("(")[0]
+                key = (name, fn, r.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _, _), v in per.items():
+        tot, cnt = out.get(name, (0.0, 0))
+        out[name] = (tot + v, cnt + 1)
+    return {k: (tot / cnt, cnt) for k, (tot, cnt) in out.items()}
+
+
+def traffic_table(fetch_dir, write_dir, f_scale, w_scale):
+    """Markdown rows: calibrated HBM read and write bytes per launch of every
+    kernel seen by both counter passes."""
+    fe = _pmc_all_kernels(fetch_dir, "FETCH_SIZE")
+    wr = _pmc_all_kernels(write_dir, "WRITE_SIZE")
+    rows = ["| Kernel | Launches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Read (MB) | Write (MB) |",
+            "|---|---|---|---|---|---|"]
+    for name in sorted(set(fe) & set(wr), key=lambda k: -fe[k][0]):
+        f_kib, nf = fe[name]
+        w_kib, _ = wr[name]
+        rows.append(f"| `{name}` | {nf} | {f_kib:.1f} | {w_kib:.1f} | {f_kib * 1024 * f_scale / 1e6:.2f} | "
+                    f"{w_kib * 1024 * w_scale / 1e6:.2f} |")
+    return "\n".join(rows)
+
+
 def traffic_summary(fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each
     scaled by what the same counter reads for the 1 GiB calibration kernel."""
@@ -745,6 +783,7 @@ def traffic_summary(fetch_dir, write_dir):
         "write_calibration": {"counter_kib_per_launch": w_cal, "true_bytes": true_bytes, "scale": w_scale},
         "dispatches": {"fetch": nf, "write": nw},
     }
+    print(traffic_table(fetch_dir, write_dir, f_scale, w_scale))
     return rec
 
 
