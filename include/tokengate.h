@@ -145,8 +145,14 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
  * caller workspace of at least tg_select_topk_workspace_size(n) bytes
  * (8448 + 12 ceil(n / 64) + 4 ceil(n / 8)), 16-byte aligned, whose contents
  * need not be initialised.  Calls that share a workspace must be ordered on one stream.
- * Budgets that keep the whole document or none of it run the one-workgroup
- * kernel of tg_select_topk instead.
+ * Documents (n - q_len) longer than 32768 tokens, which one workgroup would
+ * have to re-read block by block in every pass, run six short kernels over
+ * 2048-key chunks instead (a clear, three histogram passes, the per-chunk
+ * counts, the writes of idx), with no workgroup waiting for another;
+ * documents longer than 2^24 tokens, budgets that keep the whole document and
+ * budgets that keep none of it run the one-workgroup kernel of
+ * tg_select_topk.  Every form leaves the workspace's first 8196 bytes zero,
+ * as tg_gate_select expects.
  * Errors: as tg_select_topk; a NULL or misaligned workspace -> INVALID_ARG;
  * a workspace smaller than tg_select_topk_workspace_size(n) -> WORKSPACE. */
 TG_API int64_t tg_select_topk_workspace_size(int64_t n); /* -1 for n outside [0, 2^31) */
@@ -175,8 +181,11 @@ TG_API tg_status tg_select_topk_ws(const float* g, int64_t n, int64_t k, int64_t
  *              a previous call) gives undefined indices, never an access
  *              outside the arguments.  Calls sharing a workspace must be
  *              ordered on one stream.
- *   dtype      TG_BF16 runs the fused kernels; TG_FP32 runs the fp32 gate
- *              followed by the multi-workgroup selection (same workspace).
+ *   dtype      TG_BF16 runs the fused kernels while the document
+ *              (n - q_len) fits what the gate's last workgroup holds in LDS
+ *              (32768 tokens at hidden 256, 24576 at 128, 18432 at 64);
+ *              longer documents, and TG_FP32, run the gate followed by
+ *              tg_select_topk_ws on the same workspace (same results).
  * Errors: those of tg_gate_score and tg_select_topk_ws.
  */
 TG_API tg_status tg_gate_select(tg_dtype dtype, int64_t n, int32_t d, int32_t hidden,

@@ -28,6 +28,17 @@ constexpr int kGateBM = 128;       // tokens per workgroup
 constexpr int kGateBK = 64;        // k elements per LDS stage (128 bytes of a row)
 constexpr int kGateThreads = 512;  // 8 waves: 2 along tokens x 2 along hidden units x 2 along k
 
+// Bytes of one stage of the LDS ring (an h tile and a W1 tile, 128-byte
+// rows), and the document keys the last workgroup of the selecting form can
+// hold in the ring's three stages once the ring is free.
+template <int H>
+struct GateRing {
+  static constexpr int kStage = kGateBM * 128 + H * 128;
+  static constexpr int kPage = kStage / 4 / kCompactChunk * kCompactChunk;
+  static constexpr int kBlockTok =
+      3 * kPage < kSelMaxBlockChunks * kCompactChunk ? 3 * kPage : kSelMaxBlockChunks * kCompactChunk;
+};
+
 // LDS tile rows are 128 bytes = 8 chunks of 16 bytes.  Chunk c of row r is
 // stored at chunk slot c ^ ((r >> 1) & 7): the 16 rows read by one
 // ds_read_b128 quarter-wave then hit all 64 banks exactly once.
@@ -54,7 +65,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
   constexpr int B_DMA = H * 8 / kGateThreads;         // same for W1
   constexpr int PER_CHUNK = A_DMA + B_DMA;            // vmcnt increments per stage per wave
   constexpr int H_BYTES = kGateBM * 128;
-  constexpr int STAGE = H_BYTES + H * 128;
+  constexpr int STAGE = GateRing<H>::kStage;
   static_assert(A_DMA >= 1 && B_DMA >= 1 && (MT * NT) % 2 == 0, "tile shape");
 
   // Three separate objects, so the compiler can tell that reads of one stage
@@ -288,9 +299,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     if (!sel_publish_and_arrive<kGateThreads, true>(sel_sh, sel.ws)) return;
     // The ring is free: its three stages hold the keys while the last
     // workgroup ranks.
-    constexpr int kPage = STAGE / 4 / kCompactChunk * kCompactChunk;
-    constexpr int kBlockTok = (3 * kPage < kSelMaxBlockChunks * kCompactChunk ? 3 * kPage
-                                                                             : kSelMaxBlockChunks * kCompactChunk);
+    constexpr int kPage = GateRing<H>::kPage;
+    constexpr int kBlockTok = GateRing<H>::kBlockTok;
     SelKeys kp;
     kp.page[0] = reinterpret_cast<uint32_t*>(st0);
     kp.page[1] = reinterpret_cast<uint32_t*>(st1);
@@ -367,6 +377,10 @@ hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t
                             const void* w1, const float* b1, const float* w2, float b2, float* g,
                             float* s, hipStream_t stream) {
   return launch_gate_any<false>(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, GateSel{0, 0, nullptr}, stream);
+}
+
+int64_t gate_select_block_tokens(int hidden) {
+  return hidden == 64 ? GateRing<64>::kBlockTok : (hidden == 128 ? GateRing<128>::kBlockTok : GateRing<256>::kBlockTok);
 }
 
 hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,

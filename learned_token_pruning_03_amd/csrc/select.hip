@@ -474,6 +474,258 @@ __global__ __launch_bounds__(256) void gather_items_kernel(CompactArgs a) {
   }
 }
 
+// ---- long documents: six kernels -------------------------------------------
+// Above one LDS block of keys (kFinishBlock), one workgroup would re-read the
+// scores block by block in every pass; there the same selection runs spread
+// over ceil(doc / 2048) workgroups of 256 threads, one 2048-key chunk each, in
+// six short kernels with no grid-wide barrier:
+//   zero    clears the three histograms in the workspace;
+//   hist<0> histograms bits [31:21] of every key (LDS, then device atomics);
+//   hist<1> finds the bin holding the kd-th largest key from histogram 0 and
+//           histograms bits [20:10] of the keys in that bin;
+//   hist<2> the same one level down, bits [9:0];
+//   count   resolves T and `need` from histogram 2 and counts, per chunk, the
+//           keys above T and equal to T;
+//   write   places every kept index at its ascending slot: the chunk's offset
+//           is the sum of the counts of the chunks before it.
+// Every workgroup resolves the previous histogram itself (the same scan, the
+// same answer); workgroup 0 also stores the answer for the next kernel, each
+// pass in its own slot, so that no kernel reads a slot it writes.  The
+// workspace words these kernels use overlap the ones the fused and one-block
+// forms expect to find zero (their histogram and arrival counter, words
+// 0 .. kSelWsCounter): `write` zeroes them again on its way out, in
+// workgroup 0, which reads none of them.
+constexpr int kMwThreads = 256;
+constexpr int kMwWaves = kMwThreads / kWave;
+constexpr int kMwKpt = 8;
+constexpr int kMwChunk = kMwThreads * kMwKpt;
+constexpr int kMwH0 = 0, kMwH1 = 2048, kMwH2 = 4096;  // histogram offsets (uint32 words)
+constexpr int kMwState = 5120;                        // per pass: (prefix, need) at kMwState + 2 * pass
+constexpr int kMwCnt = 5128;                          // per chunk: (count > T, count == T)
+constexpr int64_t kSelectMwMaxDoc = int64_t(1) << 24;  // each workgroup sums at most 8191 chunk counts
+// The public workspace size (sel_ws_bytes) covers this layout for every
+// document above kFinishBlock: at the smallest such document it holds 7748
+// words against 5162 needed, and it grows by ~0.17 words per token against
+// 0.001 here.
+static_assert(kSelWsChunks + 3 * ((kFinishBlock + 1 + 63) / 64) + (kFinishBlock + 1 + 7) / 8 >=
+                  kMwCnt + 2 * ((kFinishBlock + 1 + kMwChunk - 1) / kMwChunk),
+              "workspace too small for the six-kernel form");
+
+struct MwShared {
+  uint32_t hist[2048];
+  uint32_t red[kMwWaves][2];
+  uint32_t bcast[2];
+};
+
+__device__ __forceinline__ void mw_excl_scan2(MwShared& sh, uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
+                                              uint32_t& ta, uint32_t& tb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t ia = wave_incl_scan(a, lane);
+  const uint32_t ib = wave_incl_scan(b, lane);
+  if (lane == 63) {
+    sh.red[wave][0] = ia;
+    sh.red[wave][1] = ib;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0;
+  ta = 0;
+  tb = 0;
+#pragma unroll
+  for (int w = 0; w < kMwWaves; ++w) {
+    const uint32_t xa = sh.red[w][0], xb = sh.red[w][1];
+    if (w < wave) {
+      pa += xa;
+      pb += xb;
+    }
+    ta += xa;
+    tb += xb;
+  }
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+  __syncthreads();
+}
+
+// This thread's keys (chunk blockIdx.x, KPT consecutive tokens per thread)
+// and how many of them lie inside the document.
+__device__ __forceinline__ int mw_load(const float* __restrict__ g, int doc, bool vec_ok, uint32_t (&key)[kMwKpt]) {
+  const int base = blockIdx.x * kMwChunk + threadIdx.x * kMwKpt;
+  const int nv = doc - base <= 0 ? 0 : (doc - base >= kMwKpt ? kMwKpt : doc - base);
+  if (vec_ok && nv == kMwKpt) {
+#pragma unroll
+    for (int j = 0; j < kMwKpt; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(g + base + j);
+      key[j] = order_key(v[0]);
+      key[j + 1] = order_key(v[1]);
+      key[j + 2] = order_key(v[2]);
+      key[j + 3] = order_key(v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMwKpt; ++j) key[j] = j < nv ? order_key(g[base + j]) : 0u;
+  }
+  return nv;
+}
+
+// Bin of an NB-bin histogram that holds the need-th largest counted key, and
+// how many keys of that bin are still to take.  Thread t owns NB/256
+// consecutive bins, highest first.
+template <int NB>
+__device__ __forceinline__ void mw_resolve(MwShared& sh, const uint32_t* __restrict__ h, uint32_t need,
+                                           uint32_t& bin, uint32_t& rest) {
+  constexpr int PER = NB / kMwThreads;
+  const int top = NB - 1 - (int)threadIdx.x * PER;
+  uint32_t loc[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    loc[i] = h[top - i];
+    sum += loc[i];
+  }
+  if (threadIdx.x == 0) {  // defaults, overwritten by exactly one thread below
+    sh.bcast[0] = 0u;
+    sh.bcast[1] = need;
+  }
+  uint32_t above, dummy, tot, tot2;
+  mw_excl_scan2(sh, sum, 0u, above, dummy, tot, tot2);
+  if (above < need && above + sum >= need) {
+    uint32_t cum = above;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (cum + loc[i] >= need) {
+        sh.bcast[0] = (uint32_t)(top - i);
+        sh.bcast[1] = need - cum;
+        break;
+      }
+      cum += loc[i];
+    }
+  }
+  __syncthreads();
+  bin = sh.bcast[0];
+  rest = sh.bcast[1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kMwThreads) void mw_zero_kernel(uint32_t* __restrict__ ws) {
+  for (int i = threadIdx.x; i < kMwState; i += kMwThreads) ws[i] = 0u;
+}
+
+// PASS 0: bits [31:21] of every key; PASS 1: bits [20:10] of the keys whose
+// top 11 bits equal the pass-0 bin; PASS 2: bits [9:0] below the 22-bit prefix.
+template <int PASS>
+__global__ __launch_bounds__(kMwThreads) void mw_hist_kernel(const float* __restrict__ g, int doc, int kd,
+                                                             bool vec_ok, uint32_t* __restrict__ ws) {
+  __shared__ MwShared sh;
+  constexpr int NB = PASS == 2 ? 1024 : 2048;
+  constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
+  uint32_t key[kMwKpt];
+  const int nv = mw_load(g, doc, vec_ok, key);
+  uint32_t prefix = 0;
+  if (PASS > 0) {
+    const uint32_t prev_prefix = PASS == 1 ? 0u : ws[kMwState + 0];
+    const uint32_t prev_need = PASS == 1 ? (uint32_t)kd : ws[kMwState + 1];
+    uint32_t bin, rest;
+    mw_resolve<2048>(sh, ws + (PASS == 1 ? kMwH0 : kMwH1), prev_need, bin, rest);
+    prefix = (prev_prefix << 11) | bin;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      ws[kMwState + 2 * (PASS - 1)] = prefix;
+      ws[kMwState + 2 * (PASS - 1) + 1] = rest;
+    }
+  }
+  for (int i = threadIdx.x; i < NB; i += kMwThreads) sh.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kMwKpt; ++j) {
+    const uint32_t kk = key[j];
+    const bool match = j < nv && (PASS == 0 || (kk >> (SHIFT + (PASS == 2 ? 10 : 11))) == prefix);
+    if (match) atomicAdd(&sh.hist[(kk >> SHIFT) & (NB - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* h = ws + (PASS == 0 ? kMwH0 : (PASS == 1 ? kMwH1 : kMwH2));
+  for (int i = threadIdx.x; i < NB; i += kMwThreads) {
+    const uint32_t c = sh.hist[i];
+    if (c) atomicAdd(&h[i], c);
+  }
+}
+
+// Resolves T (the kd-th largest document key) and `need` (how many keys equal
+// to T are kept); stores them (workgroup 0) and this chunk's two counts.
+__global__ __launch_bounds__(kMwThreads) void mw_count_kernel(const float* __restrict__ g, int doc, bool vec_ok,
+                                                              uint32_t* __restrict__ ws) {
+  __shared__ MwShared sh;
+  uint32_t key[kMwKpt];
+  const int nv = mw_load(g, doc, vec_ok, key);
+  uint32_t bin, rest;
+  mw_resolve<1024>(sh, ws + kMwH2, ws[kMwState + 3], bin, rest);
+  const uint32_t T = (ws[kMwState + 2] << 10) | bin;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws[kMwState + 4] = T;
+    ws[kMwState + 5] = rest;
+  }
+  uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+  for (int j = 0; j < kMwKpt; ++j)
+    if (j < nv) {
+      cgt += key[j] > T;
+      ceq += key[j] == T;
+    }
+  uint32_t egt, eeq, tgt, teq;
+  mw_excl_scan2(sh, cgt, ceq, egt, eeq, tgt, teq);
+  if (threadIdx.x == 0) {
+    ws[kMwCnt + 2 * blockIdx.x] = tgt;
+    ws[kMwCnt + 2 * blockIdx.x + 1] = teq;
+  }
+}
+
+__global__ __launch_bounds__(kMwThreads) void mw_write_kernel(const float* __restrict__ g, int doc, int kd, int q,
+                                                              bool vec_ok, const uint32_t* __restrict__ ws,
+                                                              uint32_t* __restrict__ ws_clear,
+                                                              int32_t* __restrict__ out) {
+  __shared__ MwShared sh;
+  uint32_t key[kMwKpt];
+  const int nv = mw_load(g, doc, vec_ok, key);
+  const uint32_t T = ws[kMwState + 4];
+  const uint32_t need = ws[kMwState + 5];
+  // This chunk's offset: the counts of every chunk before it.
+  uint32_t pgt = 0, peq = 0;
+  for (int c = threadIdx.x; c < (int)blockIdx.x; c += kMwThreads) {
+    pgt += ws[kMwCnt + 2 * c];
+    peq += ws[kMwCnt + 2 * c + 1];
+  }
+  uint32_t e0, e1, chunk_gt, chunk_eq;
+  mw_excl_scan2(sh, pgt, peq, e0, e1, chunk_gt, chunk_eq);
+  uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+  for (int j = 0; j < kMwKpt; ++j)
+    if (j < nv) {
+      cgt += key[j] > T;
+      ceq += key[j] == T;
+    }
+  uint32_t egt, eeq, tgt, teq;
+  mw_excl_scan2(sh, cgt, ceq, egt, eeq, tgt, teq);
+  uint32_t gt_before = chunk_gt + egt;
+  uint32_t eq_before = chunk_eq + eeq;
+  const int base = blockIdx.x * kMwChunk + threadIdx.x * kMwKpt;
+#pragma unroll
+  for (int j = 0; j < kMwKpt; ++j) {
+    if (j < nv) {
+      const uint32_t kk = key[j];
+      if (kk > T) {
+        const uint32_t slot = gt_before + min(eq_before, need);
+        if (slot < (uint32_t)kd) out[slot] = base + j;
+        ++gt_before;
+      } else if (kk == T) {
+        const uint32_t slot = gt_before + eq_before;
+        if (eq_before < need && slot < (uint32_t)kd) out[slot] = base + j;
+        ++eq_before;
+      }
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < q; i += kMwThreads) out[kd + i] = doc + i;  // protected tail
+    for (int i = threadIdx.x; i <= kSelWsCounter; i += kMwThreads) ws_clear[i] = 0u;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const float* g, int64_t n, int64_t k, int64_t q_len, const int32_t* cu_seqlens,
@@ -538,9 +790,26 @@ hipError_t launch_select_mw(const float* g, int64_t n, int64_t k, int64_t q_len,
   // Nothing to rank (budget covers the document, or only the tail is kept):
   // the one-workgroup kernel writes the identity or the tail.
   if (kd <= 0 || kd >= doc) return launch_select(g, n, k, q_len, nullptr, nullptr, 1, n, idx, nullptr, stream);
+  auto* ws = static_cast<uint32_t*>(workspace);
+  if (doc > kFinishBlock) {
+    // More chunks than the per-chunk offset sums of the six-kernel form are
+    // sized for: one workgroup does it.
+    if (doc > kSelectMwMaxDoc) return launch_select(g, n, k, q_len, nullptr, nullptr, 1, n, idx, nullptr, stream);
+    const int64_t chunks = (doc + kMwChunk - 1) / kMwChunk;
+    if (!grid_fits(chunks, kMwThreads)) return hipErrorInvalidConfiguration;
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(g) & 15u) == 0;
+    const dim3 grid((unsigned)chunks);
+    hipLaunchKernelGGL(mw_zero_kernel, dim3(1), dim3(kMwThreads), 0, stream, ws);
+    hipLaunchKernelGGL(mw_hist_kernel<0>, grid, dim3(kMwThreads), 0, stream, g, (int)doc, (int)kd, vec_ok, ws);
+    hipLaunchKernelGGL(mw_hist_kernel<1>, grid, dim3(kMwThreads), 0, stream, g, (int)doc, (int)kd, vec_ok, ws);
+    hipLaunchKernelGGL(mw_hist_kernel<2>, grid, dim3(kMwThreads), 0, stream, g, (int)doc, (int)kd, vec_ok, ws);
+    hipLaunchKernelGGL(mw_count_kernel, grid, dim3(kMwThreads), 0, stream, g, (int)doc, vec_ok, ws);
+    hipLaunchKernelGGL(mw_write_kernel, grid, dim3(kMwThreads), 0, stream, g, (int)doc, (int)kd, (int)q_len, vec_ok,
+                       ws, ws, idx);
+    return hipGetLastError();
+  }
   const int64_t blocks = (doc + kHistChunk - 1) / kHistChunk;
   if (!grid_fits(blocks, kHistThreads)) return hipErrorInvalidConfiguration;
-  auto* ws = static_cast<uint32_t*>(workspace);
   if (!ws_clean) hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, stream, ws);
   hipLaunchKernelGGL(sel_hist_finish_kernel, dim3((unsigned)blocks), dim3(kHistThreads), 0, stream, g, (int)doc,
                      (int)kd, ws);

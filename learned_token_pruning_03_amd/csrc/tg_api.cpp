@@ -129,13 +129,15 @@ static tg_status gate_select_impl(const char* what, tg_dtype dtype, int64_t n, i
   }
   const int64_t doc = n - q_len, kd = kept - q_len;
   hipError_t e;
-  if (dtype == TG_BF16 && kd > 0 && kd < doc) {
+  if (dtype == TG_BF16 && kd > 0 && kd < doc && doc <= tg::gate_select_block_tokens(hidden)) {
     e = tg::launch_gate_select_bf16(n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, k, q_len, idx, workspace, h_out,
                                     g_out, pos_out, stream);
   } else {
-    // fp32, or a budget with nothing to rank: the gate, then the selection
+    // fp32, a budget with nothing to rank, or a document longer than the
+    // gate's last workgroup holds in LDS: the gate, then the selection
     // kernels (the one-workgroup kernel writes the identity or the tail
-    // directly when kd says so), then the gather.
+    // directly when kd says so; long documents take the multi-workgroup
+    // form), then the gather.
     e = launch_gate(dtype, n, d, hidden, h, ld_h, w1, b1, w2, b2, g, s, stream);
     if (e == hipSuccess) e = tg::launch_select_mw(g, n, k, q_len, idx, workspace, true, stream);
     if (e == hipSuccess && gather)

@@ -92,7 +92,11 @@ hipError_t launch_gate_bf16(int64_t n, int d, int hidden, const void* h, int64_t
 // Gate MLP whose last workgroup also ranks the scores it wrote (bf16 only;
 // select workspace zero on entry, zero again on exit), then the compaction
 // kernel: idx, and with h_out the kept rows, gate values and positions.
-// Requires 0 < kd = min(k, n) - q_len < n - q_len.
+// Requires 0 < kd = min(k, n) - q_len < n - q_len and a document of at most
+// gate_select_block_tokens(hidden) tokens (what the last workgroup holds in
+// LDS; longer documents take the gate, the multi-workgroup select and the
+// gather instead).
+int64_t gate_select_block_tokens(int hidden);
 hipError_t launch_gate_select_bf16(int64_t n, int d, int hidden, const void* h, int64_t ld_h, const void* w1,
                                    const float* b1, const float* w2, float b2, float* g, float* s, int64_t k,
                                    int64_t q_len, int32_t* idx, void* workspace, void* h_out, float* g_out,

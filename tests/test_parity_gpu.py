@@ -224,11 +224,15 @@ def _counts_clean(ws):
     (1000, 256, 64, 300, 17, 0.0), (5000, 512, 128, 999, 0, 0.05), (4097, 2048, 256, 4096, 64, 0.05),
     (129, 64, 256, 100, 1, 0.0), (300, 2048, 256, 300, 20, 0.0), (300, 2048, 256, 1000, 20, 0.0),
     (300, 2048, 256, 20, 20, 0.0), (3, 64, 64, 2, 1, 0.0), (40000, 256, 256, 5000, 64, 0.05),
-    (70001, 128, 256, 4096, 64, 0.05)])
+    (70001, 128, 256, 4096, 64, 0.05), (32832, 256, 256, 4096, 64, 0.0), (32833, 256, 256, 4096, 64, 0.0),
+    (18464, 128, 64, 2000, 32, 0.05), (18465, 128, 64, 2000, 32, 0.05), (24608, 128, 128, 3000, 32, 0.0),
+    (24609, 128, 128, 3000, 32, 0.0)])
 def test_gate_select_parity(gpu_lib, n, d, hidden, k, q, planted):
     """Ragged row counts against the 128-row gate tiles, budgets that keep the
-    whole prompt or only the tail, and documents of one, two and three
-    32768-key chunks of the last workgroup's ranking."""
+    whole prompt or only the tail, and documents on both sides of what the
+    gate's last workgroup ranks itself (32768, 24576 and 18432 document tokens
+    at hidden 256, 128 and 64); longer documents (40000 and 70001 tokens too)
+    take the gate and the six-kernel selection."""
     _say("gate_select", n, d, hidden, k, q)
     h = W.hidden_states(n, d, torch.bfloat16, 31 + n, planted_frac=planted)
     w1, b1, w2, _ = W.gate_weights(d, hidden, torch.bfloat16, 31 + n)
