@@ -151,8 +151,9 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
  * counts, the writes of idx), with no workgroup waiting for another;
  * documents longer than 2^24 tokens, budgets that keep the whole document and
  * budgets that keep none of it run the one-workgroup kernel of
- * tg_select_topk.  Every form leaves the workspace's first 8196 bytes zero,
- * as tg_gate_select expects.
+ * tg_select_topk.  The multi-workgroup forms leave the workspace's first
+ * 8196 bytes zero, as tg_gate_select expects; the one-workgroup kernel does
+ * not touch the workspace.
  * Errors: as tg_select_topk; a NULL or misaligned workspace -> INVALID_ARG;
  * a workspace smaller than tg_select_topk_workspace_size(n) -> WORKSPACE. */
 TG_API int64_t tg_select_topk_workspace_size(int64_t n); /* -1 for n outside [0, 2^31) */
