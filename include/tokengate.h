@@ -143,7 +143,8 @@ TG_API tg_status tg_select_topk(const float* g, int64_t n, int64_t k, int64_t q_
  * finish (an arrival counter in the workspace, no waiting) ranks alone; and
  * one workgroup per 64 tokens that writes the kept indices.  It takes a
  * caller workspace of at least tg_select_topk_workspace_size(n) bytes
- * (8448 + 12 ceil(n / 64) + 4 ceil(n / 8)), 16-byte aligned, whose contents
+ * (4 (R64(2112 + 3 ceil(n / 64) + ceil(n / 8)) + R256(n)), where Rm rounds up
+ * to a multiple of m: about 4.4 n + 8.5 KB), 16-byte aligned, whose contents
  * need not be initialised.  Calls that share a workspace must be ordered on one stream.
  * Documents (n - q_len) longer than 32768 tokens, which one workgroup would
  * have to re-read block by block in every pass, run six short kernels over

@@ -37,6 +37,7 @@ struct GateRing {
   static constexpr int kPage = kStage / 4 / kCompactChunk * kCompactChunk;
   static constexpr int kBlockTok =
       3 * kPage < kSelMaxBlockChunks * kCompactChunk ? 3 * kPage : kSelMaxBlockChunks * kCompactChunk;
+  static_assert(kPage % 256 == 0 && kBlockTok % 256 == 0, "keys are copied in 256-key blocks");
 };
 
 // LDS tile rows are 128 bytes = 8 chunks of 16 bytes.  Chunk c of row r is
@@ -283,18 +284,21 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
   if (tid < kGateBM && row < n) {
     const float sc = (srow[0][tid] + srow[1][tid]) + (srow[2][tid] + srow[3][tid]) + b2;
     gv = 1.0f / (1.0f + expf(-sc));
-    if constexpr (SEL)  // read back in this kernel by the last workgroup: written past the L2
-      __hip_atomic_store(&g[row], gv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      g[row] = gv;
+    g[row] = gv;
     if (s_out) s_out[row] = sc;
   }
   if constexpr (SEL) {
     // TokenGate paper page, Figure 1(b): the selector ranks the scores the
     // gate just produced.  Top-digit counts of this workgroup's document
     // tokens go to the workspace; the last workgroup to finish selects.
+    // The order keys go to the workspace too, written past the L2: the last
+    // workgroup copies them into LDS in this kernel.
     __syncthreads();
-    if (tid < kGateBM && row < sel.doc) atomicAdd(&sel_sh.hist[order_key(gv) >> 21], 1u);
+    if (tid < kGateBM && row < sel.doc) {
+      const uint32_t key = order_key(gv);
+      atomicAdd(&sel_sh.hist[key >> 21], 1u);
+      __hip_atomic_store(&sel.ws[sel_keys_word(sel.doc) + row], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (!sel_publish_and_arrive<kGateThreads, true>(sel_sh, sel.ws)) return;
     // The ring is free: its three stages hold the keys while the last
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     kp.page[2] = reinterpret_cast<uint32_t*>(st2);
     kp.page_tokens = kPage;
     kp.block_tokens = kBlockTok;
-    select_finish<kGateThreads>(sel_sh, kp, g, sel.doc, sel.kd, sel.ws);
+    select_finish<kGateThreads>(sel_sh, kp, sel.doc, sel.kd, sel.ws);
   }
 }
 

@@ -316,26 +316,40 @@ __global__ __launch_bounds__(kHistThreads) void sel_hist_finish_kernel(const flo
   __shared__ __attribute__((aligned(16))) uint32_t keys[kFinishBlock];
   for (int i = threadIdx.x; i < kSelBins; i += kHistThreads) sh.hist[i] = 0u;
   __syncthreads();
+  // Each key is counted and also stored in the workspace, past the L2: the
+  // last workgroup copies the keys into LDS in this kernel.
+  uint32_t* const wkeys = ws + sel_keys_word(doc);
   const int base = blockIdx.x * kHistChunk + threadIdx.x * kHistKpt;
+  uint32_t key[kHistKpt];
   if (base + kHistKpt <= doc && (reinterpret_cast<uintptr_t>(g) & 15u) == 0) {
     const f32x4 v0 = *reinterpret_cast<const f32x4*>(g + base);
     const f32x4 v1 = *reinterpret_cast<const f32x4*>(g + base + 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) atomicAdd(&sh.hist[order_key(v0[j]) >> 21], 1u);
+    for (int j = 0; j < 4; ++j) {
+      key[j] = order_key(v0[j]);
+      key[4 + j] = order_key(v1[j]);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) atomicAdd(&sh.hist[order_key(v1[j]) >> 21], 1u);
+    for (int j = 0; j < kHistKpt; ++j) {
+      atomicAdd(&sh.hist[key[j] >> 21], 1u);
+      __hip_atomic_store(&wkeys[base + j], key[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < kHistKpt; ++j)
-      if (base + j < doc) atomicAdd(&sh.hist[order_key(g[base + j]) >> 21], 1u);
+      if (base + j < doc) {
+        const uint32_t kj = order_key(g[base + j]);
+        atomicAdd(&sh.hist[kj >> 21], 1u);
+        __hip_atomic_store(&wkeys[base + j], kj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
   }
   __syncthreads();
-  if (!sel_publish_and_arrive<kHistThreads, false>(sh, ws)) return;
+  if (!sel_publish_and_arrive<kHistThreads, true>(sh, ws)) return;
   SelKeys kp;
   kp.page[0] = kp.page[1] = kp.page[2] = keys;
   kp.page_tokens = kFinishBlock;
   kp.block_tokens = kFinishBlock;
-  select_finish<kHistThreads>(sh, kp, g, doc, kd, ws);
+  select_finish<kHistThreads>(sh, kp, doc, kd, ws);
 }
 
 // Where each kept token goes, from T, need and the chunk counts:

@@ -23,7 +23,11 @@
 //               keys above T, then equal to T, in the chunks before it;
 //   then        copy items, chunk * 16 + part: part p of chunk c stands for
 //               the chunk's kept tokens of rank 8p .. 8p + 7 (at most 8
-//               rows per item, however the kept tokens cluster).
+//               rows per item, however the kept tokens cluster);
+//   [sel_keys_word(doc)]  the order key of every document score, written by
+//               the workgroup that counted it (past the L2), so that the
+//               last workgroup copies them straight into LDS; padded to a
+//               whole number of 256-key blocks.
 // The kernels after it read T, need, the chunk counts and the items: one
 // workgroup per chunk (indices only) or per item (indices and rows) places
 // its kept tokens without any global scan.
@@ -48,8 +52,10 @@ __host__ __device__ inline int64_t sel_chunks(int64_t n) { return (n + kCompactC
 // ceil(kept_c / 8) <= chunks + kept / 8.
 __host__ __device__ inline int64_t sel_max_items(int64_t n) { return sel_chunks(n) + (n + kItemRows - 1) / kItemRows; }
 __host__ __device__ inline int64_t sel_items_word(int64_t n) { return kSelWsChunks + 2 * sel_chunks(n); }
+__host__ __device__ inline int64_t sel_keys_word(int64_t n) { return (sel_items_word(n) + sel_max_items(n) + 63) / 64 * 64; }
+__host__ __device__ inline int64_t sel_keys_words(int64_t n) { return (n + 255) / 256 * 256; }
 // Workspace bytes for a prompt of n tokens.
-inline int64_t sel_ws_bytes(int64_t n) { return (sel_items_word(n) + sel_max_items(n)) * (int64_t)sizeof(uint32_t); }
+inline int64_t sel_ws_bytes(int64_t n) { return (sel_keys_word(n) + sel_keys_words(n)) * (int64_t)sizeof(uint32_t); }
 
 // Unsigned order of the key == rank order of the score: NaN -> 0 (lowest),
 // -0 -> +0, negatives reversed below positives.
@@ -71,8 +77,8 @@ struct SelFinishShared {
 // A block of keys held in LDS, in up to three pages (the gate keeps them in
 // the three stages of its ring).  The 64-token chunk starting at token i of
 // the block sits in page i / page_tokens.  block_tokens and page_tokens are
-// multiples of 64; block_tokens is at most 64 * kSelMaxBlockChunks and
-// 3 * page_tokens.
+// multiples of 256 (the keys are copied in 256-key blocks); block_tokens is at
+// most 64 * kSelMaxBlockChunks and 3 * page_tokens.
 struct SelKeys {
   uint32_t* page[3];
   int page_tokens;
@@ -225,14 +231,13 @@ __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, 
 // No agent-scope fence on the way: on this multi-XCD part such a fence writes
 // back the whole L2 of the XCD, which costs microseconds per workgroup.
 // Instead everything another workgroup will read is written past the L2
-// (device atomics for the counts, agent-scope atomic stores for scores
-// written in the same kernel), each thread waits until its own writes have
-// completed (vmcnt 0) before the barrier, and only then does one thread
-// count the workgroup in.  When the scores were written by this kernel, the
-// last workgroup then drops its L2's copies (an agent-scope acquire: an
-// invalidate, no write-back) before it reads them.
-// ACQUIRE: the last workgroup reads scores that other workgroups of the same
-// kernel wrote; without it the scores come from an earlier kernel.
+// (device atomics for the counts, agent-scope atomic stores for the keys),
+// each thread waits until its own writes have completed (vmcnt 0) before the
+// barrier, and only then does one thread count the workgroup in.  The last
+// workgroup then drops its L2's copies (an agent-scope acquire: an
+// invalidate, no write-back) before it reads the keys.
+// ACQUIRE: the last workgroup reads data that other workgroups of the same
+// kernel wrote; without it, only data from an earlier kernel.
 template <int THREADS, bool ACQUIRE>
 __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint32_t* __restrict__ ws) {
   for (int i = threadIdx.x; i < kSelBins; i += THREADS) {
@@ -250,8 +255,9 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 }
 
 // The rest of the selection, in one workgroup of THREADS threads, once the
-// workspace holds the top-digit histogram of all `doc` document keys of
-// g[0, doc):
+// workspace holds the top-digit histogram of all `doc` document keys and the
+// keys themselves (at sel_keys_word(doc), written past the L2 by the
+// workgroups that counted them):
 //   - the top digit's bin holding the kd-th largest key, from the histogram
 //     (rebuilt here from the keys if its total is not `doc`);
 //   - bits 20..10, then 9..0, of the keys still in play, counted in LDS: the
@@ -268,55 +274,46 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 // thread visits only the keys still in play (a bit mask over its chunk), and
 // every memory access of a phase is issued before the first wait.
 template <int THREADS>
-__device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys& kp, const float* __restrict__ g,
-                                              int doc, int kd, uint32_t* __restrict__ ws) {
+__device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys& kp, int doc, int kd,
+                                              uint32_t* __restrict__ ws) {
   constexpr int PER = kSelBins / THREADS;
   constexpr int kMaxIt = kSelMaxBlockChunks * kCompactChunk / (4 * THREADS);  // 16-byte loads per thread per block
   static_assert(PER * THREADS == kSelBins && kMaxIt >= 1 && THREADS >= kSelMaxBlockChunks, "block shape");
+  static_assert(kMaxIt * (THREADS / kWave) * 256 == kSelMaxBlockChunks * kCompactChunk, "one copy per 256 keys");
   const int tid = threadIdx.x;
   const int B = kp.block_tokens;
   const int nblocks = (doc + B - 1) / B;
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(g) & 15u) == 0;
+  const uint32_t* const keys = ws + sel_keys_word(doc);
   const bool owner = tid < B / kCompactChunk;  // this thread owns a chunk of every block
   uint32_t* const mine = sel_key_ptr(kp, owner ? tid * kCompactChunk : 0);
   auto slot_of = [](uint32_t* chunk, int t, int grp) __attribute__((always_inline)) {
     return chunk + 4 * ((grp + t) & 15);
   };
 
-  // Keys of block c into LDS: coalesced 16-byte loads, all in flight before
-  // the barrier that lets the previous block's readers finish, each stored
-  // in its owner's chunk; a partial vector at the document's end (or scores
-  // not 16-byte aligned) goes through a short scalar loop.  Keys past the
-  // document are never read back (every loop below stops at the chunk's
-  // valid count).
+  // Keys of block c into LDS by global -> LDS copies (no register round
+  // trip), all in flight at once after the barrier that lets the previous
+  // block's readers finish.  A wave's copy moves a 256-key block (4 chunks);
+  // lane l fills slot l % 16 of chunk l / 16, so it fetches the group of 4
+  // keys that the chunk's rotation puts in that slot.  Blocks past the
+  // document are not copied; keys past it in the last block are stale and
+  // never read back (every loop below stops at the chunk's valid count).
   int cur = -1;
   auto load_block = [&](int c) __attribute__((always_inline)) {
     const int base = c * B;
-    f32x4 v[kMaxIt];
-#pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) {
-      const int i = 4 * (tid + it * THREADS);
-      if (vec_ok && i < B && base + i + 4 <= doc) v[it] = *reinterpret_cast<const f32x4*>(g + base + i);
-    }
     __syncthreads();
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cc = (tid & 63) >> 4, j = tid & 15;
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it) {
-      const int i = 4 * (tid + it * THREADS);
-      const int o = i / kCompactChunk;
-      if (vec_ok && i < B && base + i + 4 <= doc)
-        *reinterpret_cast<u32x4*>(slot_of(sel_key_ptr(kp, o * kCompactChunk), o, (i % kCompactChunk) / 4)) =
-            u32x4{order_key(v[it][0]), order_key(v[it][1]), order_key(v[it][2]), order_key(v[it][3])};
-    }
-#pragma unroll 1
-    for (int it = 0; it < kMaxIt; ++it) {
-      const int i = 4 * (tid + it * THREADS);
-      if (i < B && base + i < doc && !(vec_ok && base + i + 4 <= doc)) {
-        const int o = i / kCompactChunk;
-        uint32_t* kq = slot_of(sel_key_ptr(kp, o * kCompactChunk), o, (i % kCompactChunk) / 4);
-#pragma unroll 1
-        for (int e = 0; e < 4 && base + i + e < doc; ++e) kq[e] = order_key(g[base + i + e]);
+      const int wb = it * (THREADS / kWave) + wv;  // this wave's 256-key block
+      const int i0 = wb * 256;
+      if (i0 < B && base + i0 < doc) {
+        const int t = 4 * wb + cc;  // the chunk (and owner thread) this lane's slot belongs to
+        dma16(keys + base + i0 + cc * kCompactChunk + 4 * ((j - t) & 15),
+              (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)sel_key_ptr(kp, i0));
       }
     }
+    wait_vm<0>();
     __syncthreads();
     cur = c;
   };

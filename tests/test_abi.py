@@ -221,9 +221,15 @@ def test_grids_beyond_one_dispatch_are_refused_before_any_hip_call(lib):
 def test_select_ws_validation_without_a_gpu(lib):
     ws = lib.tg_select_topk_workspace_size(32768)
     # an 11-bit histogram, an arrival counter, T, need and the item count; two counts per 64-token
-    # chunk; then up to one copy item per chunk plus one per 8 tokens
-    assert ws == (2048 + 64) * 4 + 8 * (32768 // 64) + 4 * (32768 // 64 + 32768 // 8)
-    assert lib.tg_select_topk_workspace_size(100) == (2048 + 64) * 4 + 8 * 2 + 4 * (2 + 13)
+    # chunk; then up to one copy item per chunk plus one per 8 tokens; then, from a 64-word
+    # boundary, one order key per token, padded to a whole number of 256-key blocks
+    def words(n):
+        chunks = -(-n // 64)
+        head = 2048 + 64 + 2 * chunks + chunks + -(-n // 8)
+        return -(-head // 64) * 64 + -(-n // 256) * 256
+    assert ws == 4 * words(32768) == 4 * (7744 + 32768)
+    assert lib.tg_select_topk_workspace_size(100) == 4 * words(100) == 4 * (2176 + 256)
+    assert lib.tg_select_topk_workspace_size(131072) == 4 * words(131072)
     assert lib.tg_select_topk_workspace_size(-1) == -1
     ok = tg.TG_ERR_INVALID_ARG
     assert lib.tg_select_topk_ws(FAKE, 32768, 4096, 64, FAKE, FAKE, ws - 4, None) == tg.TG_ERR_WORKSPACE
