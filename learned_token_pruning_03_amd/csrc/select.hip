@@ -15,6 +15,12 @@
 // key, with a 2048-bin LDS histogram and a block suffix scan per pass.  A
 // final block scan over (count > T, count == T) places every kept index at
 // its ascending slot; the first `need` tokens equal to T (by index) are kept.
+//
+// Also here: the multi-workgroup forms of the same selection (up to 32768
+// document tokens: a histogram kernel whose last workgroup ranks, then a
+// compaction; longer documents: six short kernels), and the compaction that
+// also copies the kept rows, used after the gate that ranks in its last
+// workgroup.
 #include "select_core.h"
 
 namespace tg {
@@ -290,12 +296,14 @@ void launch_kpt(const float* g, int n, int64_t k, int q, const int32_t* cu, cons
 }
 
 // ---- several workgroups per prompt ------------------------------------------
-// The same selection in three short kernels with no grid-wide barrier:
+// Up to one LDS block of document keys (kFinishBlock), the same selection in
+// three short kernels with no grid-wide barrier:
 //   sel_clear_kernel        zeroes the workspace's histogram and counter;
 //   sel_hist_finish_kernel  ceil(doc / 4096) workgroups of 512 threads count
-//                           the top 11 bits of 8 keys per thread in LDS and
-//                           add them to the workspace; the last workgroup to
-//                           arrive ranks alone (select_finish): T, need and
+//                           the top 11 bits of 8 keys per thread in LDS, add
+//                           them to the workspace and store the keys there;
+//                           the last workgroup to arrive copies the keys into
+//                           LDS and ranks alone (select_finish): T, need and
 //                           the counts before every 64-token chunk;
 //   compact_kernel          one workgroup per 64-token chunk writes the kept
 //                           indices of its chunk.
