@@ -16,9 +16,7 @@
  * The path, per prompt:  gate score (all N tokens) -> top-K select (question
  * tail always kept) -> gather of the kept rows, gate values and positions ->
  * per upper layer: RoPE + compact KV cache, then token-gated causal GQA
- * attention over the K kept tokens (tg_rope_kv and tg_gated_attn; or
- * tg_rope_kv for the keys only and tg_rope_gated_attn, which rotates the
- * queries as it loads them).
+ * attention over the K kept tokens.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -275,12 +273,11 @@ TG_API tg_status tg_gather_varlen(tg_dtype dtype, const int32_t* cu_seqlens,
  * cos(p*theta_0..theta_{dh/2-1}) then sin(...), computed in fp64 on the device.
  *
  * tg_rope_kv, per kept token i at position pos[i]:
- *   q[i]        rotated in place             q [n_kept, hq, dh], or NULL
+ *   q[i]        rotated in place             q [n_kept, hq, dh]
  *   k_cache[i]  = rotated k[i]               k, k_cache [n_kept, hkv, dh]
  *   v_cache[i]  = v[i]  (copy; skipped when v_cache == v)
  * dh: a multiple of 16, at most 256.  A position outside [0, max_pos) gives
- * zero outputs for that token.  q == NULL rotates no queries: the form to use
- * with tg_rope_gated_attn, which rotates them as it loads them.
+ * zero outputs for that token.
  * ------------------------------------------------------------------------- */
 TG_API tg_status tg_rope_table(float* cos_sin, int64_t max_pos, int32_t dh, double base,
                                hipStream_t stream);
@@ -315,8 +312,7 @@ TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t 
  *           both dtypes apply the causal mask by kept index (key j visible
  *           to query i iff j <= i), which is the mask above whenever the
  *           positions strictly increase; the values of pos are not read
- *           here (tg_rope_gated_attn reads them to rotate its queries;
- *           tg_check_positions verifies the precondition on the device).
+ *           (tg_check_positions verifies the precondition on the device).
  *           Must be non-NULL.
  *   o       [n_kept, hq, dh] output, dtype.
  *   lse     [hq, n_kept] fp32 output (natural log), or NULL.
@@ -358,29 +354,6 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
                                   int32_t dh, float scale, const void* q, const void* k,
                                   const void* v, const float* g, const float* head_gain,
                                   const int32_t* pos, void* o, float* lse, hipStream_t stream);
-
-/* ---------------------------------------------------------------------------
- * Gated attention that applies the queries' RoPE itself.  The same result as
- * tg_rope_kv rotating q in place followed by tg_gated_attn_ex on the rotated
- * q (the same fp32 rotation, rounded once to dtype), without writing the
- * rotated queries back to memory and reading them again: pair it with
- * tg_rope_kv(q = NULL), which then rotates the keys and fills the caches.
- *
- *   q           [total, hq, dh] UNROTATED queries; not modified.
- *   pos         [total] int32 original positions: query i is rotated at
- *               pos[i] (the causal mask still compares kept indices, as in
- *               tg_gated_attn).  A position outside [0, max_pos) gives that
- *               query zeros, as tg_rope_kv does.
- *   cos_sin     [max_pos, dh] fp32 table of tg_rope_table (device, 16-byte
- *               aligned).     max_pos: its rows, in [0, 2^31).
- *   Other arguments and errors as tg_gated_attn_ex.
- * ------------------------------------------------------------------------- */
-TG_API tg_status tg_rope_gated_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
-                                    int64_t max_seqlen, int64_t total, int32_t hq, int32_t hkv,
-                                    int32_t dh, float scale, const void* q, const void* k,
-                                    const void* v, const float* g, const float* head_gain,
-                                    const int32_t* pos, const float* cos_sin, int64_t max_pos, void* o,
-                                    float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode attention over the compact KV cache.  [aitu] section 3: past the

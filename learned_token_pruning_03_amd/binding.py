@@ -57,9 +57,6 @@ SIGNATURES = {
                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "tg_gated_attn_ex": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp,
                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
-    "tg_rope_gated_attn": ([ctypes.c_int, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_f32, _c_vp,
-                            _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp],
-                           ctypes.c_int),
     "tg_linear": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64,
                    _c_vp], ctypes.c_int),
     "tg_swiglu": ([ctypes.c_int, _c_i64, _c_i32, _c_i32, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
@@ -372,24 +369,17 @@ def tg_rope_table(max_pos: int, dh: int, base: float, device, out: Optional[torc
     return out
 
 
-def tg_rope_kv(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,
-               cos_sin: torch.Tensor, k_cache: Optional[torch.Tensor] = None,
-               v_cache: Optional[torch.Tensor] = None, hq: Optional[int] = None):
-    """Rotates q in place; returns (q, k_cache, v_cache).  q=None rotates the
-    keys only (queries left to tg_rope_gated_attn); hq is then the query head
-    count the call reports (default: hkv)."""
+def tg_rope_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor,
+               k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None):
+    """Rotates q in place; returns (q, k_cache, v_cache)."""
     lib = load_library()
-    _need(k.dim() == 3, "k must be [n, hkv, dh]")
-    n, hkv, dh = k.shape
-    if q is not None:
-        _need(q.dim() == 3 and q.shape[0] == n and q.shape[2] == dh, "q must be [n, hq, dh]")
-        hq = q.shape[1]
-        _need(q.is_contiguous() and q.dtype == k.dtype, "q must be contiguous and share k's dtype")
-    elif hq is None:
-        hq = hkv
-    _need(k.is_contiguous() and v.is_contiguous(), "k, v must be contiguous")
-    _need(v.dtype == k.dtype, "k and v must share a dtype")
-    _need(tuple(v.shape) == (n, hkv, dh), "k and v must be [n, hkv, dh]")
+    _need(q.dim() == 3, "q must be [n, hq, dh]")
+    n, hq, dh = q.shape
+    hkv = k.shape[1] if k.dim() == 3 else -1
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share a dtype")
+    _need(k.dim() == 3 and tuple(k.shape) == (n, hkv, dh) and tuple(v.shape) == (n, hkv, dh),
+          "k and v must be [n, hkv, dh]")
     _vec(pos, n, torch.int32, "pos")
     _need(cos_sin.dim() == 2 and cos_sin.shape[1] == dh and cos_sin.dtype == torch.float32 and
           cos_sin.is_contiguous(), "cos_sin must be a contiguous fp32 [max_pos, dh] table")
@@ -399,9 +389,9 @@ def tg_rope_kv(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, pos:
         v_cache = torch.empty_like(v)
     _like(k_cache, k.shape, k.dtype, "k_cache")
     _like(v_cache, v.shape, v.dtype, "v_cache")
-    _check("tg_rope_kv", lib.tg_rope_kv(_dtype_code(k), n, int(hq), hkv, dh, _ptr(pos), _ptr(cos_sin),
+    _check("tg_rope_kv", lib.tg_rope_kv(_dtype_code(q), n, hq, hkv, dh, _ptr(pos), _ptr(cos_sin),
                                         cos_sin.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
-                                        _ptr(v_cache), _stream(k)))
+                                        _ptr(v_cache), _stream(q)))
     return q, k_cache, v_cache
 
 
@@ -479,38 +469,6 @@ def tg_gated_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: O
                lib.tg_gated_attn_varlen(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv,
                                         dh, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(pos), _ptr(o),
                                         _ptr(lse), _stream(q)))
-    return (o, lse) if (want_lse or lse is not None) else o
-
-
-def tg_rope_gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
-                       pos: torch.Tensor, cos_sin: torch.Tensor, scale: Optional[float] = None,
-                       o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       want_lse: bool = False, head_gain: Optional[torch.Tensor] = None,
-                       cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None):
-    """Gated attention on UNROTATED queries: each query is rotated at pos[i]
-    with the cos_sin table as it is loaded (q is not modified).  k, v are the
-    caches tg_rope_kv(q=None, ...) fills.  cu_seqlens/max_seqlen: a packed
-    ragged batch as in tg_gated_attn_varlen."""
-    lib = load_library()
-    total, hq, hkv, dh = _check_attn_operands(q, k, v, g, pos, head_gain, q.shape[0] if q.dim() == 3 else 0)
-    _need(cos_sin.dim() == 2 and cos_sin.shape[1] == dh and cos_sin.dtype == torch.float32 and
-          cos_sin.is_contiguous(), "cos_sin must be a contiguous fp32 [max_pos, dh] table")
-    batch = 1
-    if cu_seqlens is not None:
-        batch = cu_seqlens.numel() - 1
-        _vec(cu_seqlens, batch + 1, torch.int32, "cu_seqlens")
-        _need(max_seqlen is not None and 0 <= int(max_seqlen) and (batch == 0 or int(max_seqlen) <= total or
-                                                                      total == 0),
-              "max_seqlen must lie in [0, total rows]")
-    else:
-        max_seqlen = total
-    if scale is None:
-        scale = dh ** -0.5
-    o, lse = _attn_outputs(q, o, lse, want_lse, hq, total)
-    _check("tg_rope_gated_attn",
-           lib.tg_rope_gated_attn(_dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), total, hq, hkv, dh,
-                                  float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(head_gain), _ptr(pos),
-                                  _ptr(cos_sin), cos_sin.shape[0], _ptr(o), _ptr(lse), _stream(q)))
     return (o, lse) if (want_lse or lse is not None) else o
 
 

@@ -59,10 +59,6 @@ struct AttnArgs {
   int hq;
   int hkv;
   float scale_log2;
-  // RoPE of the queries as they are loaded (tg_rope_gated_attn): the cos/sin
-  // table [rope_max_pos, DH] of tg_rope_table, or NULL for rotated queries.
-  const float* rope_cs;
-  int64_t rope_max_pos;
 };
 
 template <int DH>
@@ -152,9 +148,6 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     L = a.cu[blockIdx.y + 1] - (int)s0;
   }
   const int ntiles = (L + C::BM - 1) / C::BM;
-  // Positions of this lane's query in the two tiles (RoPE on load), read at
-  // the start so that only the first tile's table reads wait for them.
-  int qpos[2] = {0, 0};
   // The short tile's keys are a prefix of the long tile's, so the bias table
   // built for the long tile serves both.  The tile body is a lambda called
   // twice rather than a loop: a loop keeps its values live across the back
@@ -264,24 +257,6 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   if (1 < niter) issue(kbase, off_k, 2 + grp, k_addr[1]);
   if (0 < niter) issue(vbase, off_v, grp, v_addr[0]);
   if (2 < niter) issue_g(2);
-  // RoPE on load: the table row of this lane's query position (pairs
-  // (i, i + DH/2); this lane holds i = 16 ks + 8 half + e of both halves).
-  // Issued after the copies, so that the wait for the position does not hold
-  // them back.
-  f32x4 rc[DH / 32][2], rs[DH / 32][2];
-  bool rope_ok = false;
-  if (a.rope_cs) {
-    const int p = qpos[pass];
-    rope_ok = p >= 0 && p < a.rope_max_pos;
-    const float* row = a.rope_cs + (int64_t)(rope_ok ? p : 0) * DH;
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        rc[ks][hh] = *reinterpret_cast<const f32x4*>(row + ks * 16 + half * 8 + 4 * hh);
-        rs[ks][hh] = *reinterpret_cast<const f32x4*>(row + DH / 2 + ks * 16 + half * 8 + 4 * hh);
-      }
-  }
   {
     // Q, g and the gate values of tile 0 have landed once at most the two
     // batches are outstanding; the copies may not have.
@@ -318,18 +293,6 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   // oacc[MD/2, MD) in the final merge with compile-time indices only (a
   // runtime index would move the accumulators to scratch memory).
   const int mdx = grp == 0 ? 0 : C::MD / 2;
-  if (a.rope_cs) {  // the same rotation and rounding as tg_rope_kv; zeros off the table
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y1, y2;
-        rope_pair((float)qf[ks][e], (float)qf[ks + DH / 32][e], rc[ks][e >> 2][e & 3], rs[ks][e >> 2][e & 3], y1,
-                  y2);
-        qf[ks][e] = (__bf16)(rope_ok ? y1 : 0.0f);
-        qf[ks + DH / 32][e] = (__bf16)(rope_ok ? y2 : 0.0f);
-      }
-  }
   __syncthreads();  // bias table complete
 
   {
@@ -578,11 +541,6 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   };
   const int mt0 = ntiles - 1 - pair;
   if (pair >= (ntiles + 1) / 2) return;  // pairs past this prompt's tiles
-  if (a.rope_cs) {
-    const int qw = (wave & 3) * 32 + (lane & 31);
-    qpos[0] = a.pos[s0 + min(mt0 * C::BM + qw, L - 1)];
-    if (pair < mt0) qpos[1] = a.pos[s0 + min(pair * C::BM + qw, L - 1)];
-  }
   tile_body(mt0, true);
   if (pair >= mt0) return;
   __syncthreads();  // the next tile's copies reuse the LDS of this tile's merge
@@ -594,14 +552,12 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
 // natural-base online softmax with the ln g bias.  Causal by kept index, as the
 // bf16 kernels: key j is visible to query i iff j <= i, which is the mask on
 // original positions whenever they strictly increase.
-template <int DH, bool ROPE>
+template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ q,
                                                       const float* __restrict__ k,
                                                       const float* __restrict__ v,
                                                       const float* __restrict__ g,
                                                       const float* __restrict__ head_gain,
-                                                      const int32_t* __restrict__ pos,
-                                                      const float* __restrict__ rope_cs, int64_t rope_max_pos,
                                                       float* __restrict__ o, float* __restrict__ lse,
                                                       const int32_t* __restrict__ cu, int total, int hq,
                                                       int hkv, float scale) {
@@ -624,27 +580,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   const int qrow = qi < L ? qi : L - 1;
   float qv[DH];
   const float* qp = q + ((s0 + qrow) * hq + head) * DH;
-  if (ROPE) {  // RoPE on load, as tg_rope_kv would rotate the query
-    const int p = pos[s0 + qrow];
-    const bool ok = p >= 0 && p < rope_max_pos;
-    const float* row = rope_cs + (int64_t)(ok ? p : 0) * DH;
-    // Eight pairs at a time: the whole row of q and of the table at once
-    // would not fit next to the output accumulators.
 #pragma unroll
-    for (int d0 = 0; d0 < DH / 2; d0 += 8) {
-#pragma unroll
-      for (int d = d0; d < d0 + 8; ++d) {
-        float y1, y2;
-        rope_pair(qp[d], qp[d + DH / 2], row[d], row[DH / 2 + d], y1, y2);
-        qv[d] = ok ? y1 : 0.0f;
-        qv[d + DH / 2] = ok ? y2 : 0.0f;
-      }
-      asm volatile("" ::: "memory");  // keeps the next group's loads below this one
-    }
-  } else {
-#pragma unroll
-    for (int d = 0; d < DH; ++d) qv[d] = qp[d];
-  }
+  for (int d = 0; d < DH; ++d) qv[d] = qp[d];
   float m = -INFINITY, l = 0.0f;
   float ov[DH];
 #pragma unroll
@@ -694,8 +631,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch, int64_t max_seqlen,
                             int hq, int hkv, int dh, float scale, const void* q, const void* k,
                             const void* v, const float* g, const float* head_gain, const int32_t* pos,
-                            const float* rope_cs, int64_t rope_max_pos, void* o, float* lse,
-                            hipStream_t stream) {
+                            void* o, float* lse, hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint8_t*>(q);
   a.k = static_cast<const uint8_t*>(k);
@@ -710,8 +646,6 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
   a.hq = hq;
   a.hkv = hkv;
   a.scale_log2 = scale * kLog2e;
-  a.rope_cs = rope_cs;
-  a.rope_max_pos = rope_max_pos;
   const int64_t ntiles = (max_seqlen + 127) / 128;
   const int64_t npairs = (ntiles + 1) / 2;
   if (!grid_fits(npairs * hq, 512, cu_seqlens ? batch : 1)) return hipErrorInvalidConfiguration;
@@ -737,25 +671,16 @@ hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
 
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch, int64_t max_seqlen,
                            int hq, int hkv, int dh, float scale, const float* q, const float* k,
-                           const float* v, const float* g, const float* head_gain, const int32_t* pos,
-                           const float* rope_cs, int64_t rope_max_pos, float* o, float* lse,
-                           hipStream_t stream) {
+                           const float* v, const float* g, const float* head_gain, float* o,
+                           float* lse, hipStream_t stream) {
   if (!grid_fits((max_seqlen + 63) / 64, 64, hq, cu_seqlens ? batch : 1)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((max_seqlen + 63) / 64), (unsigned)hq, cu_seqlens ? (unsigned)batch : 1u);
-  // Rotating queries on load takes its own instantiation: the rotation's
-  // registers would otherwise spill in the plain form at head dim 128.
-  if (dh == 128 && rope_cs)
-    hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos,
-                       rope_cs, rope_max_pos, o, lse, cu_seqlens, (int)total, hq, hkv, scale);
-  else if (dh == 128)
-    hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos,
-                       rope_cs, rope_max_pos, o, lse, cu_seqlens, (int)total, hq, hkv, scale);
-  else if (rope_cs)
-    hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos,
-                       rope_cs, rope_max_pos, o, lse, cu_seqlens, (int)total, hq, hkv, scale);
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, o,
+                       lse, cu_seqlens, (int)total, hq, hkv, scale);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(64), 0, stream, q, k, v, g, head_gain, pos,
-                       rope_cs, rope_max_pos, o, lse, cu_seqlens, (int)total, hq, hkv, scale);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, g, head_gain, o,
+                       lse, cu_seqlens, (int)total, hq, hkv, scale);
   return hipGetLastError();
 }
 

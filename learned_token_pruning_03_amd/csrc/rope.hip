@@ -8,10 +8,6 @@
 // uses rotate-half RoPE (pairs (i, i + dh/2), angle pos * base^(-2i/dh)) at
 // each kept token's position in the original prompt.
 //
-// With q == NULL the kernel rotates keys and copies values only: the queries
-// are then rotated by the attention kernel as it loads them
-// (tg_rope_gated_attn), which saves writing them back and reading them again.
-//
 // The cos/sin table is built once per (max_pos, dh, base) in fp64 on the
 // device and stored as fp32; the rotation itself runs in fp32 and rounds once
 // to the storage type.  One workgroup per kept token: it rotates the token's
@@ -92,7 +88,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(int hq, int hkv, int dh,
   const bool ok = p >= 0 && p < max_pos;
   const int half = dh / 2;
   const int pchunks = half / 8;                 // 8-pair chunks per head
-  const int q_units = q ? hq * pchunks : 0;     // no queries: keys and values only
+  const int q_units = hq * pchunks;
   const int k_units = hkv * pchunks;
   const int v_units = (int)((int64_t)hkv * dh * ES / 16);
   const int64_t row_bytes = (int64_t)dh * ES;
@@ -120,7 +116,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(int hq, int hkv, int dh,
         for (int i = 0; i < 8; ++i) {
           const float co = i < 4 ? c0[i] : c1[i - 4];
           const float si = i < 4 ? s0[i] : s1[i - 4];
-          rope_pair(x1[i], x2[i], co, si, y1[i], y2[i]);
+          y1[i] = x1[i] * co - x2[i] * si;
+          y2[i] = x2[i] * co + x1[i] * si;
         }
       } else {
 #pragma unroll

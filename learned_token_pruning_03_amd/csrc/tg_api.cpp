@@ -284,9 +284,9 @@ TG_API tg_status tg_rope_kv(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t 
   if (hq <= 0 || hkv <= 0) return fail(TG_ERR_INVALID_ARG, "rope_kv: head counts must be positive");
   if (dh <= 0 || dh % 16 != 0 || dh > 256) return fail(TG_ERR_UNSUPPORTED, "rope_kv: dh=%d must be a multiple of 16, <= 256", dh);
   if (n_kept == 0) return ok();
-  if (!pos || !cos_sin || !k || !v || !k_cache || !v_cache)  // q NULL: keys and values only
+  if (!pos || !cos_sin || !q || !k || !v || !k_cache || !v_cache)
     return fail(TG_ERR_INVALID_ARG, "rope_kv: NULL pointer argument");
-  if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(cos_sin))
     return fail(TG_ERR_INVALID_ARG, "rope_kv: tensors must be 16-byte aligned");
   return from_hip(tg::launch_rope_kv(elem_size(dtype), n_kept, hq, hkv, dh, pos, cos_sin, max_pos, q, k,
@@ -316,14 +316,14 @@ static hipError_t dispatch_attn(tg_dtype dtype, int64_t total, const int32_t* cu
                                 int64_t max_seqlen, int32_t hq, int32_t hkv, int32_t dh, float scale,
                                 const void* q, const void* k, const void* v, const float* g,
                                 const float* head_gain, const int32_t* pos, void* o, float* lse,
-                                hipStream_t stream, const float* rope_cs = nullptr, int64_t rope_max_pos = 0) {
+                                hipStream_t stream) {
   if (dtype == TG_BF16)
     return tg::launch_attn_bf16(total, cu, batch, max_seqlen, hq, hkv, dh, scale, q, k, v, g, head_gain,
-                                pos, rope_cs, rope_max_pos, o, lse, stream);
+                                pos, o, lse, stream);
   return tg::launch_attn_f32(total, cu, batch, max_seqlen, hq, hkv, dh, scale,
                              static_cast<const float*>(q), static_cast<const float*>(k),
-                             static_cast<const float*>(v), g, head_gain, pos, rope_cs, rope_max_pos,
-                             static_cast<float*>(o), lse, stream);
+                             static_cast<const float*>(v), g, head_gain, static_cast<float*>(o),
+                             lse, stream);
 }
 
 TG_API tg_status tg_gated_attn(tg_dtype dtype, int64_t n_kept, int32_t hq, int32_t hkv, int32_t dh,
@@ -377,33 +377,6 @@ TG_API tg_status tg_gated_attn_ex(tg_dtype dtype, const int32_t* cu_seqlens, int
   return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
                                 g, head_gain, pos, o, lse, stream),
                   "attn_ex");
-}
-
-TG_API tg_status tg_rope_gated_attn(tg_dtype dtype, const int32_t* cu_seqlens, int32_t batch,
-                                    int64_t max_seqlen, int64_t total, int32_t hq, int32_t hkv,
-                                    int32_t dh, float scale, const void* q, const void* k,
-                                    const void* v, const float* g, const float* head_gain,
-                                    const int32_t* pos, const float* cos_sin, int64_t max_pos, void* o,
-                                    float* lse, hipStream_t stream) {
-  if (total < 0 || total > kMaxI32) return fail(TG_ERR_INVALID_ARG, "rope_attn: total out of range");
-  if (max_pos < 0 || max_pos > kMaxI32) return fail(TG_ERR_INVALID_ARG, "rope_attn: max_pos out of range");
-  if (cu_seqlens) {
-    if (batch < 0 || max_seqlen < 0 || max_seqlen > kMaxI32)
-      return fail(TG_ERR_INVALID_ARG, "rope_attn: batch or max_seqlen out of range");
-    if (batch == 0 || total == 0 || max_seqlen == 0) return ok();
-    if (batch > kMaxGridYZ) return fail(TG_ERR_UNSUPPORTED, "rope_attn: batch above %d", kMaxGridYZ);
-  } else {
-    batch = 1;
-    max_seqlen = total;
-    if (total == 0) return ok();
-  }
-  tg_status st = check_attn(dtype, max_seqlen, hq, hkv, dh, scale, q, k, v, g, pos, o);
-  if (st != TG_OK) return st;
-  if (!cos_sin) return fail(TG_ERR_INVALID_ARG, "rope_attn: NULL cos_sin");
-  if (!aligned16(cos_sin)) return fail(TG_ERR_INVALID_ARG, "rope_attn: cos_sin must be 16-byte aligned");
-  return from_hip(dispatch_attn(dtype, total, cu_seqlens, batch, max_seqlen, hq, hkv, dh, scale, q, k, v,
-                                g, head_gain, pos, o, lse, stream, cos_sin, max_pos),
-                  "rope_attn");
 }
 
 // ---------------------------------------------------------------------------

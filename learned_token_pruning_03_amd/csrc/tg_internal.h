@@ -33,15 +33,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Rotate-half RoPE of one (x1, x2) pair, x1 from the first half of a head and
-// x2 from the second, with the table's cos and sin of the pair's angle.  One
-// definition, so tg_rope_kv and the attention kernels that rotate their
-// queries on load compute the same fp32 values.
-__device__ __forceinline__ void rope_pair(float x1, float x2, float co, float si, float& y1, float& y2) {
-  y1 = x1 * co - x2 * si;
-  y2 = x2 * co + x1 * si;
-}
-
 // 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's bytes land at
 // LDS address m0 + 16 l.  Written as asm so that the compiler's wait-count
 // pass does not track it: once copies stay in flight across a loop back-edge
@@ -144,19 +135,16 @@ hipError_t launch_rope_kv(int elem_bytes, int64_t n_kept, int hq, int hkv, int d
                           const void* k, const void* v, void* k_cache, void* v_cache,
                           hipStream_t stream);
 
-// rope_cs: the cos/sin table [rope_max_pos, dh] to rotate each query at its
-// position pos[i] as it is loaded (q holds unrotated queries), or NULL (q
-// already rotated; the bf16 kernels then never read pos).
 hipError_t launch_attn_bf16(int64_t total, const int32_t* cu_seqlens, int batch,
                             int64_t max_seqlen, int hq, int hkv, int dh, float scale,
                             const void* q, const void* k, const void* v, const float* g,
-                            const float* head_gain, const int32_t* pos, const float* rope_cs,
-                            int64_t rope_max_pos, void* o, float* lse, hipStream_t stream);
+                            const float* head_gain, const int32_t* pos, void* o, float* lse,
+                            hipStream_t stream);
 hipError_t launch_attn_f32(int64_t total, const int32_t* cu_seqlens, int batch,
                            int64_t max_seqlen, int hq, int hkv, int dh, float scale,
                            const float* q, const float* k, const float* v, const float* g,
-                           const float* head_gain, const int32_t* pos, const float* rope_cs,
-                           int64_t rope_max_pos, float* o, float* lse, hipStream_t stream);
+                           const float* head_gain, float* o, float* lse,
+                           hipStream_t stream);
 
 // Decode attention: keys per split-K block, and the launch of the split and
 // combine kernels (workspace: batch * hq * nsplit * (dh + 2) floats).

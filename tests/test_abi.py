@@ -27,7 +27,6 @@ def test_header_declares_the_expected_entry_points():
     for name in ("tg_gate_score", "tg_gate_select", "tg_gate_select_gather", "tg_select_topk", "tg_select_topk_varlen", "tg_select_topk_workspace_size",
                  "tg_select_topk_ws", "tg_gather", "tg_gather_varlen",
                  "tg_rope_table", "tg_rope_kv", "tg_gated_attn", "tg_gated_attn_varlen", "tg_gated_attn_ex",
-                 "tg_rope_gated_attn",
                  "tg_decode_attn_workspace_size", "tg_decode_attn",
                  "tg_linear", "tg_swiglu", "tg_qkv_proj", "tg_check_positions",
                  "tg_status_string",
@@ -105,31 +104,6 @@ def test_attn_ex_validation_without_a_gpu(lib):
                                 FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # NULL pos
     assert lib.tg_gated_attn_ex(tg.TG_BF16, None, 1, 16, -1, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
                                 FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # negative total
-
-
-def test_rope_attn_validation_without_a_gpu(lib):
-    # tg_rope_gated_attn(dtype, cu, batch, max_seqlen, total, hq, hkv, dh, scale, q, k, v, g, head_gain, pos,
-    #                    cos_sin, max_pos, o, lse, stream): the arguments of tg_gated_attn_ex plus the table.
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 0, 16, 8, 128, 0.1, None, None, None, None, None, None,
-                                  None, 0, None, None, None) == tg.TG_OK  # nothing to do
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 16, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
-                                  None, 10, FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # NULL table
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 16, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
-                                  FAKE, -1, FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # negative max_pos
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 16, 16, 8, 96, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
-                                  FAKE, 10, FAKE, None, None) == tg.TG_ERR_UNSUPPORTED  # head dim
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 16, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, None,
-                                  FAKE, 10, FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # NULL pos
-    assert lib.tg_rope_gated_attn(tg.TG_BF16, None, 1, 16, 16, 16, 8, 128, 0.1, FAKE, FAKE, FAKE, None, None, FAKE,
-                                  FAKE + 4, 10, FAKE, None, None) == tg.TG_ERR_INVALID_ARG  # misaligned table
-
-
-def test_rope_kv_takes_no_queries_but_needs_the_rest(lib):
-    # q NULL: keys and values only; the other pointers stay mandatory.  A zero-row call is a no-op.
-    assert lib.tg_rope_kv(tg.TG_BF16, 0, 16, 8, 128, None, None, 10, None, None, None, None, None,
-                          None) == tg.TG_OK
-    assert lib.tg_rope_kv(tg.TG_BF16, 4, 16, 8, 128, FAKE, FAKE, 10, None, None, FAKE, FAKE, FAKE,
-                          None) == tg.TG_ERR_INVALID_ARG  # NULL k
 
 
 def test_decode_validation_without_a_gpu(lib):

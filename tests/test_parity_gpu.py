@@ -628,106 +628,6 @@ def test_attn_masks_by_kept_index_not_position_values(gpu_lib, dtype, tol):
     assert np.max(np.abs(lse_bad - wl)) <= 1e-3
 
 
-# ----------------------------------------------------------------------------- attention with RoPE on load
-ROPE_BASE, ROPE_MAX_POS = 1e6, 131072
-
-
-def _rope_attn_case(n, hq, hkv, dh, dtype, seed, gkind="uniform"):
-    """Unrotated q, rotated key cache (the caller's tg_rope_kv(q=None) half) and
-    positions spread over the table."""
-    q, k, v, g, _ = _attn_inputs(n, hq, hkv, dh, dtype, seed, gkind)
-    pos = np.sort(np.random.default_rng(seed + 1).choice(ROPE_MAX_POS, n, replace=False)).astype(np.int32)
-    pos[0] = 0
-    if n > 1:
-        pos[-1] = ROPE_MAX_POS - 1
-    kc = torch.from_numpy(ref_rope(k, pos, ROPE_BASE)).to(dtype)
-    return q, kc, v, g, torch.from_numpy(pos)
-
-
-@pytest.mark.parametrize("dtype,n,hq,hkv,dh,gkind,tol",
-                         [(torch.bfloat16, 300, 16, 8, 128, "wide", 2e-2), (torch.bfloat16, 129, 4, 2, 64, "edge", 2e-2),
-                          (torch.bfloat16, 1, 4, 4, 128, "uniform", 2e-2),
-                          (torch.bfloat16, 640, 6, 3, 128, "uniform", 2e-2),
-                          (torch.float32, 200, 4, 2, 64, "edge", 1e-4), (torch.float32, 77, 2, 1, 128, "wide", 1e-4)])
-def test_rope_gated_attn_parity(gpu_lib, dtype, n, hq, hkv, dh, gkind, tol):
-    """The fused call against the oracle's rotation followed by its attention."""
-    _say("rope attn", dtype, n, hq, hkv, dh, gkind)
-    q, kc, v, g, pos = _rope_attn_case(n, hq, hkv, dh, dtype, n + dh, gkind)
-    table = gpu_lib.tg_rope_table(ROPE_MAX_POS, dh, ROPE_BASE, DEV)
-    qd = q.to(DEV)
-    o, lse = gpu_lib.tg_rope_gated_attn(qd, kc.to(DEV), v.to(DEV), g.to(DEV), pos.to(DEV), table, want_lse=True)
-    torch.cuda.synchronize()
-    assert torch.equal(qd.cpu(), q)  # the queries are not modified
-    wo, wl = ref_attn(ref_rope(q, pos.numpy(), ROPE_BASE), kc, v, g, pos.numpy())
-    err = float(np.max(np.abs(o.cpu().double().numpy() - wo)))
-    _say("  max abs err o", err)
-    assert err <= tol
-    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= (1e-3 if dtype == torch.bfloat16 else 1e-4)
-
-
-@pytest.mark.parametrize("dtype,dh", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128)])
-def test_rope_gated_attn_equals_rope_then_attention(gpu_lib, dtype, dh):
-    """Rotating on load rounds the same fp32 rotation as tg_rope_kv, so the
-    fused call and the two calls (queries rotated in place, then attention)
-    give the same bits; the key cache tg_rope_kv(q=None) fills is the one it
-    fills with queries."""
-    n, hq, hkv = 515, 8, 2
-    q, k, v, g, _ = _attn_inputs(n, hq, hkv, dh, dtype, 91, "wide")
-    pos = torch.from_numpy(np.sort(np.random.default_rng(92).choice(ROPE_MAX_POS, n, replace=False)).astype(np.int32))
-    table = gpu_lib.tg_rope_table(ROPE_MAX_POS, dh, ROPE_BASE, DEV)
-    qd, kd, vd, gd, pd = (t.to(DEV) for t in (q, k, v, g, pos))
-    _, kc0, vc0 = gpu_lib.tg_rope_kv(None, kd, vd, pd, table, hq=hq)
-    o_fused = gpu_lib.tg_rope_gated_attn(qd, kc0, vc0, gd, pd, table)
-    q2 = qd.clone()
-    _, kc1, vc1 = gpu_lib.tg_rope_kv(q2, kd, vd, pd, table)
-    o_two = gpu_lib.tg_gated_attn(q2, kc1, vc1, gd, pd)
-    torch.cuda.synchronize()
-    assert torch.equal(kc0, kc1) and torch.equal(vc0, vc1)
-    assert torch.equal(o_fused, o_two)
-
-
-def test_rope_gated_attn_varlen_with_head_gain_and_positions_off_the_table(gpu_lib):
-    """Packed batch with per-head gains; rows whose position lies outside the
-    table are rotated to zero queries (as tg_rope_kv zeroes them)."""
-    lens = [256, 1, 100, 0, 129]
-    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    total = int(cu[-1])
-    hq, hkv, dh, max_pos = 4, 2, 128, 4096
-    q, k, v, g, _ = _attn_inputs(total, hq, hkv, dh, torch.bfloat16, 45, "wide")
-    pos = np.concatenate([np.arange(m) * 37 for m in lens]).astype(np.int32)  # reaches past max_pos
-    pos[3] = -5
-    table = gpu_lib.tg_rope_table(max_pos, dh, ROPE_BASE, DEV)
-    gain = _gains(hq, 45)
-    o, lse = gpu_lib.tg_rope_gated_attn(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), torch.from_numpy(pos).to(DEV),
-                                        table, want_lse=True, head_gain=gain.to(DEV),
-                                        cu_seqlens=torch.from_numpy(cu).to(DEV), max_seqlen=max(lens))
-    torch.cuda.synchronize()
-    off = (pos < 0) | (pos >= max_pos)
-    assert off.any() and (~off).any()
-    qr = ref_rope(q, np.where(off, 0, pos), ROPE_BASE)
-    qr[off] = 0.0
-    # The mask compares kept indices (the rotation alone reads the positions).
-    rank = np.concatenate([np.arange(m) for m in lens])
-    wo, wl = ref_attn_varlen(qr, k, v, g, rank, cu, head_gain=gain.numpy())
-    assert np.max(np.abs(o.cpu().double().numpy() - wo)) <= 2e-2
-    assert np.max(np.abs(lse.cpu().double().numpy() - wl)) <= 1e-3
-
-
-def test_rope_kv_without_queries(gpu_lib):
-    """q=None: the caches as with queries, no query touched."""
-    n, hq, hkv, dh = 300, 8, 4, 128
-    q, k, v = W.qkv(n, hq, hkv, dh, 1.0 / dh, torch.bfloat16, 23)
-    pos = torch.from_numpy(np.sort(np.random.default_rng(23).choice(ROPE_MAX_POS, n, replace=False)).astype(np.int32))
-    table = gpu_lib.tg_rope_table(ROPE_MAX_POS, dh, ROPE_BASE, DEV)
-    kd, vd, pd = k.to(DEV), v.to(DEV), pos.to(DEV)
-    _, kc, vc = gpu_lib.tg_rope_kv(None, kd, vd, pd, table, hq=hq)
-    torch.cuda.synchronize()
-    want = ref_rope(k, pos.numpy(), ROPE_BASE)
-    got = kc.cpu().double().numpy()
-    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
-    assert torch.equal(vc.cpu(), v)
-
-
 # ----------------------------------------------------------------------------- end to end
 def test_end_to_end_qwen_32k(gpu_lib):
     """The full path at the 32k workload: each stage checked against the oracle
