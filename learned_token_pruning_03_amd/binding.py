@@ -108,7 +108,12 @@ def _check(func: str, status: int) -> None:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of t for the C ABI (which takes device pointers only)."""
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return t.data_ptr()
 
 
 def _stream(t: torch.Tensor) -> Optional[int]:
@@ -133,17 +138,19 @@ def _need(cond: bool, msg: str) -> None:
 # The C ABI takes raw pointers and no buffer lengths, so these checks are the
 # only guard against a call that would read or write past a tensor.
 def _vec(t: Optional[torch.Tensor], n: int, dtype: torch.dtype, name: str) -> None:
-    """t is None, or a contiguous tensor of `dtype` with at least n elements."""
+    """t is None, or a contiguous GPU tensor of `dtype` with at least n elements."""
     if t is None:
         return
     _need(t.dtype == dtype and t.is_contiguous() and t.numel() >= n,
           f"{name} must be a contiguous {dtype} tensor with at least {n} elements")
+    _need(t.device.type == "cuda", f"{name} must live on the GPU")
 
 
 def _like(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
-    """t is a contiguous tensor of exactly `shape` and `dtype`."""
+    """t is a contiguous GPU tensor of exactly `shape` and `dtype`."""
     _need(tuple(t.shape) == tuple(shape) and t.dtype == dtype and t.is_contiguous(),
           f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    _need(t.device.type == "cuda", f"{name} must live on the GPU")
 
 
 # ---------------------------------------------------------------------------

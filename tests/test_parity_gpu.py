@@ -628,6 +628,21 @@ def test_attn_masks_by_kept_index_not_position_values(gpu_lib, dtype, tol):
     assert np.max(np.abs(lse_bad - wl)) <= 1e-3
 
 
+def test_binding_refuses_host_buffers_next_to_device_ones(gpu_lib):
+    """A host tensor among device tensors is refused before any launch: the C
+    ABI takes raw pointers and would hand the kernel a host address."""
+    q, k, v, g, pos = _attn_inputs(64, 4, 2, 64, torch.bfloat16, 3)
+    qd, kd, vd, gd, pd = (t.to(DEV) for t in (q, k, v, g, pos))
+    with pytest.raises(ValueError):
+        gpu_lib.tg_gated_attn(qd, kd, vd, g, pd)  # gate values on the host
+    with pytest.raises(ValueError):
+        gpu_lib.tg_gated_attn(qd, kd, vd, gd, pos)  # positions on the host
+    with pytest.raises(ValueError):
+        gpu_lib.tg_gated_attn(qd, kd, vd, gd, pd, o=torch.empty_like(q))  # output on the host
+    with pytest.raises(ValueError):
+        gpu_lib.tg_gated_attn(qd, k, vd, gd, pd)  # keys on the host
+
+
 # ----------------------------------------------------------------------------- end to end
 def test_end_to_end_qwen_32k(gpu_lib):
     """The full path at the 32k workload: each stage checked against the oracle
