@@ -270,9 +270,9 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 // Thread t owns chunk t of the block held in LDS (its 16 groups of 4 keys
 // rotated by t, so that the 16 lanes of a quarter-wave read 16 different
 // bank groups); a document of several blocks is re-read once per pass.  A
-// single workgroup runs this once, so every phase is a short loop: each
-// thread visits only the keys still in play (a bit mask over its chunk), and
-// every memory access of a phase is issued before the first wait.
+// single workgroup runs this once: each phase reads the thread's 64 keys into
+// registers with all its LDS reads in flight, then works from the registers
+// (a counting pass issues one predicated LDS atomic per key still in play).
 template <int THREADS>
 __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys& kp, int doc, int kd,
                                               uint32_t* __restrict__ ws) {
@@ -327,7 +327,6 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
 #pragma unroll
     for (int i = 0; i < 16; ++i) k[i] = *reinterpret_cast<const u32x4*>(slot_of(mine, tid, i));
   };
-  auto key_at = [&](int j) __attribute__((always_inline)) { return slot_of(mine, tid, j >> 2)[j & 3]; };
 
   // ---- top digit: the published histogram (read past the L2), into LDS,
   // with the first block's keys in flight at the same time.
@@ -383,25 +382,18 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
       // tested one by one.
       const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
       if (phase < 3) {
-        // The keys of the chunk still in play, then one atomic per such key.
-        uint64_t live = 0;
+        // One predicated LDS atomic per key still in play, straight from the
+        // registers: a loop over the live keys alone would run as many rounds
+        // as the fullest chunk of the wave holds, each round waiting for an
+        // LDS read of its key (kept tokens cluster, so one chunk can hold many).
         const int sh_known = phase == 0 ? 0 : 32 - known;
         const uint32_t want = phase == 0 ? 0u : prefix;
         const uint32_t shmask = phase == 0 ? 0u : 0xffffffffu;
 #pragma unroll
         for (int j = 0; j < 64; ++j) {
           const uint32_t kk = k[j >> 2][j & 3];
-          live |= (uint64_t)(((kk >> sh_known) & shmask) == want) << j;
-        }
-        live &= valid;
-#pragma unroll 1
-        while (__ballot(live != 0ull) != 0ull) {
-          if (live != 0ull) {
-            const int j = __builtin_ctzll(live);
-            live &= live - 1ull;
-            const uint32_t kk = key_at(j);
+          if (j < nv && ((kk >> sh_known) & shmask) == want)
             atomicAdd(&sh.hist[phase == 0 ? kk >> 21 : (kk >> shift) & mask], 1u);
-          }
         }
         continue;
       }
