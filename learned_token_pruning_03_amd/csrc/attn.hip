@@ -489,23 +489,35 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
 
     // ---- merge the two groups' partial results, normalise, store ----
     // Group 0 finishes d-blocks md < MD/2, group 1 blocks md >= MD/2: each
-    // hands the other half of its partial O^T (and its m, l) across LDS.
+    // hands the other half of its partial O^T (and its m, l) across LDS in
+    // 16-byte pieces.  The normalised bf16 tile is staged in LDS (the second
+    // V buffer, unused by the merge) and written out as whole rows: written
+    // straight from the accumulators, every store instruction would touch 32
+    // query rows.
     __syncthreads();
     constexpr int HM = C::MD / 2;
-    float* to_g0 = reinterpret_cast<float*>(k_s0);  // group 1's rows md < HM
-    float* to_g1 = reinterpret_cast<float*>(k_s1);  // group 0's rows md >= HM
+    f32x4* to_g0 = reinterpret_cast<f32x4*>(k_s0);  // group 1's rows md < HM
+    f32x4* to_g1 = reinterpret_cast<f32x4*>(k_s1);  // group 0's rows md >= HM
     float* scr_m = reinterpret_cast<float*>(v_s0);
     float* scr_l = scr_m + 8 * 64;
     {
-      float* out = grp == 0 ? to_g1 : to_g0;
+      f32x4* out = grp == 0 ? to_g1 : to_g0;
 #pragma unroll
       for (int h = 0; h < HM; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) out[(w4 * (HM * 16) + h * 16 + r) * 64 + lane] = oacc[HM + h][r];
+        for (int rq = 0; rq < 4; ++rq)
+          out[(w4 * (HM * 4) + h * 4 + rq) * 64 + lane] =
+              f32x4{oacc[HM + h][4 * rq], oacc[HM + h][4 * rq + 1], oacc[HM + h][4 * rq + 2], oacc[HM + h][4 * rq + 3]};
       scr_m[wave * 64 + lane] = m;
       scr_l[wave * 64 + lane] = lsum;
     }
     __syncthreads();
+    // Output tile in LDS: row ql = query row0 + ql, DH/8 chunks of 16 bytes,
+    // chunk c stored at c ^ (ql % (DH/8)).
+    uint8_t* const stage = v_s1;
+    constexpr int ROWB = DH * 2;
+    constexpr int CMASK = DH / 8 - 1;
+    static_assert(C::BM * ROWB <= 2 * KB, "output tile fits in one V buffer pair");
     {
       const float m1 = scr_m[(wave ^ 4) * 64 + lane];
       const float l1 = scr_l[(wave ^ 4) * 64 + lane];
@@ -515,26 +527,37 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       float l = lsum * a0 + l1 * a1;
       l += __shfl_xor(l, 32, kWave);
       const float inv = 1.0f / l;
-      const float* in = grp == 0 ? to_g0 : to_g1;
+      const f32x4* in = grp == 0 ? to_g0 : to_g1;
       const int md0 = grp == 0 ? 0 : HM;
-      if (qi < L) {
-        uint8_t* op = a.o + (((s0 + qi) * hq + head) * DH) * 2;
+      const int ql = w4 * 32 + r32;
 #pragma unroll
-        for (int h = 0; h < HM; ++h) {
-          const f32x16& keep = oacc[h];
+      for (int h = 0; h < HM; ++h) {
+        const f32x16& keep = oacc[h];
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float ov[4];
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 iv = in[(w4 * (HM * 4) + h * 4 + rq) * 64 + lane];
+          float ov[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rq + e;
-              ov[e] = (keep[r] * a0 + in[(w4 * (HM * 16) + h * 16 + r) * 64 + lane] * a1) * inv;
-            }
-            const u32x2 packed = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-            *reinterpret_cast<u32x2*>(op + ((md0 + h) * 32 + 8 * rq + 4 * half) * 2) = packed;
-          }
+          for (int e = 0; e < 4; ++e) ov[e] = (keep[4 * rq + e] * a0 + iv[e] * a1) * inv;
+          const u32x2 packed = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+          const int c = (md0 + h) * 4 + rq;  // the 16-byte chunk holding dh 8c .. 8c+7
+          *reinterpret_cast<u32x2*>(stage + ql * ROWB + ((c ^ (ql & CMASK)) << 4) + 8 * half) = packed;
         }
-        if (a.lse && grp == 0 && half == 0) a.lse[(int64_t)head * a.total + s0 + qi] = (mt_ + log2f(l)) * kLn2;
+      }
+      if (a.lse && grp == 0 && half == 0 && qi < L)
+        a.lse[(int64_t)head * a.total + s0 + qi] = (mt_ + log2f(l)) * kLn2;
+    }
+    __syncthreads();
+    {
+      // 16 consecutive threads write one query row (DH = 128) with 16-byte stores.
+      constexpr int CPR_O = DH / 8;
+#pragma unroll
+      for (int x = tid; x < C::BM * CPR_O; x += 512) {
+        const int ql = x / CPR_O, c = x % CPR_O;
+        if (row0 + ql < L) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(stage + ql * ROWB + ((c ^ (ql & CMASK)) << 4));
+          *reinterpret_cast<u32x4*>(a.o + (((s0 + row0 + ql) * hq + head) * DH) * 2 + c * 16) = val;
+        }
       }
     }
   }
