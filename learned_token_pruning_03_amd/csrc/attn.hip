@@ -167,7 +167,6 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
 
   const int row0 = mt * C::BM;
   const int qi = row0 + w4 * 32 + r32;
-  const int qrow = qi < L ? qi : L - 1;
   const int kend = min(L, row0 + C::BM);
   const int n_kt = (kend + BN - 1) / BN;
   const int niter = grp == 0 ? (n_kt + 1) / 2 : n_kt / 2;  // this group's tiles, kt = 2t + grp
@@ -224,14 +223,23 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   };
   auto g_count = [&](int t) __attribute__((always_inline)) { return (g_wave && t < niter) ? 1 : 0; };
 
-  // ---- prologue: Q fragments and gate values (register loads) first, then
-  // the first copies, so the register loads can be waited for while the
-  // copies keep landing.
-  const uint8_t* qp = a.q + (((s0 + qrow) * hq + head) * DH) * 2;
-  bf16x8 qf[DH / 16];
+  // ---- prologue: the Q tile and the gate values first, then the first K/V
+  // copies, so that one wait covers Q and g while the copies keep landing.
+  // The Q tile goes into the second V buffer (not written before the first
+  // VALU slot) by global -> LDS copies of whole rows, laid out like a K tile:
+  // loaded into registers directly, every load instruction would touch 32
+  // query rows.  Copy i of this thread fills 16-byte slot P = 512 i + tid:
+  // row P / CPR, holding logical chunk (P % CPR) ^ swz_k(row); rows past the
+  // prompt re-read its last row.
+  static_assert(C::BM * C::CPR % 512 == 0 && C::BM * C::ROW <= 2 * KB, "Q tile copies");
 #pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (ks * 16 + half * 8) * 2);
+  for (int i = 0; i < C::BM * C::CPR / 512; ++i) {
+    const int P = i * 512 + tid;
+    const int r = P / C::CPR;
+    const int src_row = min(row0 + r, L - 1);
+    dma16(a.q + (((s0 + src_row) * hq + head) * DH) * 2 + ((P % C::CPR) ^ C::swz_k(r)) * 16,
+          lds_addr(v_s1) + (i * 512 + wave * 64) * 16);
+  }
   // Bias table, in units of the raw score (log2 g / c), for every key this
   // query tile can see (rounded up to whole key tiles); keys past the prompt
   // get -inf.
@@ -293,7 +301,14 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
   // oacc[MD/2, MD) in the final merge with compile-time indices only (a
   // runtime index would move the accumulators to scratch memory).
   const int mdx = grp == 0 ? 0 : C::MD / 2;
-  __syncthreads();  // bias table complete
+  __syncthreads();  // bias table and Q tile complete
+  // Q fragments, read like those of a K tile; waited for here, before the
+  // first VALU slot's copies can reach the buffer.
+  bf16x8 qf[DH / 16];
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(v_s1 + w4 * 32 * C::ROW + (koff0 ^ (ks << 5)));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
   {
     auto batch_count = [&](int b) __attribute__((always_inline)) {
