@@ -62,8 +62,16 @@ def parse_args(argv=None):
 
 
 def _file_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 prefix of a C++/HIP source's code: comments, trailing spaces and
+    blank lines are dropped first, so that a comment edit does not void the
+    counters taken on the same code."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 # The stand-alone multi-workgroup select (a clearing kernel, a histogram kernel

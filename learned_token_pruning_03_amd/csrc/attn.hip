@@ -27,6 +27,9 @@
 //    XOR-swizzled 256-byte rows); the V^T operand is read with
 //    ds_read_b64_tr_b16, the transposing LDS read, so V needs no
 //    transposition pass;
+//  * the Q tile arrives the same way (into a V buffer not yet in use) and
+//    the normalised output tile leaves through LDS as whole rows, so no load
+//    or store instruction touches 32 query rows at once;
 //  * the causal test runs only on tiles reaching past a wave's first query;
 //  * the online softmax keeps a reference maximum per query that only moves
 //    when a logit exceeds it by more than 8 (log2 units), so the O rescale is
