@@ -140,6 +140,16 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
 
   const int half = lane >> 5;  // which 8-element k group of the MFMA operand
   const int r32 = lane & 31;
+  // b1 and w2 at this lane's hidden units, for the epilogue.  Loaded here,
+  // ahead of the first copies, so that they have long arrived when the
+  // epilogue needs them (loaded there, each tile waited for its own loads).
+  float bias_u[NT], wout_u[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int unit = wn * (H / 2) + j * 32 + r32;
+    bias_u[j] = b1 ? b1[unit] : 0.0f;
+    wout_u[j] = w2[unit];
+  }
 
   // This wave takes sub-steps 2 kh and 2 kh + 1 of every 64-wide chunk; its
   // partner (same tile, other kh) takes the other two.  Both fragment sets are
@@ -249,9 +259,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         if (((i * NT + j) & 1) == kh) {
-          const int unit = wn * (H / 2) + j * 32 + r32;
-          const float bias = b1 ? b1[unit] : 0.0f;
-          const float wout = w2[unit];
+          const float bias = bias_u[j];
+          const float wout = wout_u[j];
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const f32x4 o = in[(q * 4 + r4) * kWave + lane];
@@ -267,17 +276,30 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
           ++q;
         }
   }
-  // Sum over the 32 lanes that share a token (same `half`).
+  // Sum over the 32 lanes that share a token (same `half`), on the DPP lane
+  // network: within each 16-lane row, adds across lane pairs (xor 1), lane
+  // pairs of quads (xor 2), mirrored half-rows and mirrored rows leave the
+  // row's sum in all its lanes; then every row adds lane 15 of the row before
+  // it (row_bcast:15), so lanes 31 and 63 hold the sums of their halves.  Each
+  // step is one add with a DPP source; a shuffle per step would go through
+  // the LDS and wait for it.
+  auto dpp_add = [](float v, auto ctrl_tag) __attribute__((always_inline)) {
+    constexpr int ctrl = decltype(ctrl_tag)::value;
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
+  };
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = part[i][r];
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      v = dpp_add(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+      v = dpp_add(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+      v = dpp_add(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+      v = dpp_add(v, std::integral_constant<int, 0x140>{});  // row_mirror
+      v = dpp_add(v, std::integral_constant<int, 0x142>{});  // row_bcast:15 (rows 0 and 2 unused after it)
       part[i][r] = v;
     }
-  if (r32 == 0) {
+  if (r32 == 31) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
