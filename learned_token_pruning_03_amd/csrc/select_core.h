@@ -68,8 +68,9 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 constexpr int kSelMaxBlockChunks = 512;  // 64-token chunks per block of keys held in LDS
 
-struct SelFinishShared {
-  uint32_t hist[kSelBins];
+struct alignas(16) SelFinishShared {
+  uint32_t hist[kSelBins];  // filled by 16-byte global -> LDS copies: 16-byte aligned
+  uint32_t sink[kWave];  // per-lane target of the counting atomics of keys not in play (never read)
   uint32_t red[16][2];
   uint32_t bcast[4];
 };
@@ -114,6 +115,25 @@ __device__ __forceinline__ uint32_t sel_wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Barrier for data exchanged through LDS only: each wave waits for its own
+// LDS accesses, then meets the others.  __syncthreads would also wait for
+// every global access in flight (key copies still landing, stores).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Waits until at most n (0 <= n <= N) of this wave's memory operations are
+// outstanding; n is the same for the whole wave.
+template <int N>
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N)
+      wait_vm<N>();
+    else
+      wait_vm_n<N - 1>(n);
+  }
+}
+
 // Block-wide exclusive scan of two counters in thread order; also returns
 // the block totals.  Ends with a barrier, so `red` can be reused at once.
 template <int THREADS>
@@ -129,7 +149,7 @@ __device__ __forceinline__ void sel_block_scan2(SelFinishShared& sh, uint32_t a,
     sh.red[wave][0] = ia;
     sh.red[wave][1] = ib;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t pa = 0, pb = 0;
   ta = 0;
   tb = 0;
@@ -145,7 +165,7 @@ __device__ __forceinline__ void sel_block_scan2(SelFinishShared& sh, uint32_t a,
   }
   ea = pa + ia - a;
   eb = pb + ib - b;
-  __syncthreads();
+  lds_barrier();
 }
 
 // Block-wide exclusive scan of three counters with one LDS round trip; also
@@ -164,7 +184,7 @@ __device__ __forceinline__ void sel_block_scan3(SelFinishShared& sh, const uint3
 #pragma unroll
     for (int c = 0; c < 3; ++c) (&sh.red[0][0])[3 * wave + c] = inc[c];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
     uint32_t pre = 0, t = 0;
@@ -177,23 +197,25 @@ __device__ __forceinline__ void sel_block_scan3(SelFinishShared& sh, const uint3
     ex[c] = pre + inc[c] - v[c];
     tot[c] = t;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // In sh.hist (kSelBins bins, counts of the keys still in play), the bin that
 // holds the need-th largest key, how many keys of that bin are still to take
 // (rest) and how many keys the bin holds (count).  Thread t owns
 // kSelBins / THREADS consecutive bins, highest first.
+// bin0_extra: counts in bin 0 that are not keys still in play (padding),
+// taken out as the bins are read.
 template <int THREADS>
 __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, uint32_t& bin, uint32_t& rest,
-                                            uint32_t& count, uint32_t* total = nullptr) {
+                                            uint32_t& count, uint32_t* total = nullptr, uint32_t bin0_extra = 0u) {
   constexpr int PER = kSelBins / THREADS;
   static_assert(PER >= 1 && PER * THREADS == kSelBins, "bins per thread");
   const int top = kSelBins - 1 - (int)threadIdx.x * PER;
   uint32_t loc[PER], sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    loc[i] = sh.hist[top - i];
+    loc[i] = sh.hist[top - i] - (top - i == 0 ? bin0_extra : 0u);
     sum += loc[i];
   }
   if (threadIdx.x == 0) {  // defaults, overwritten by exactly one thread below
@@ -217,11 +239,11 @@ __device__ __forceinline__ void sel_resolve(SelFinishShared& sh, uint32_t need, 
       cum += loc[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   bin = sh.bcast[0];
   rest = sh.bcast[1];
   count = sh.bcast[3];
-  __syncthreads();
+  lds_barrier();
 }
 
 // Adds this workgroup's counts (sh.hist) to the workspace histogram, then
@@ -273,6 +295,13 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 // single workgroup runs this once: each phase reads the thread's 64 keys into
 // registers with all its LDS reads in flight, then works from the registers
 // (a counting pass issues one predicated LDS atomic per key still in play).
+// Chunks wholly past the document take no part; in the one chunk the
+// document ends in, the keys past its end are set to 0 (the key of NaN) in
+// registers, so no pass tests a key's index; wherever a pass counts key 0
+// (histogram bin 0 of a prefix that is itself 0, or T == 0) those padding
+// keys are taken back out.  Each histogram pass is compiled
+// for its own digit (a phase known only at run time would make every key pay
+// for both digit extractions and a select).
 template <int THREADS>
 __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys& kp, int doc, int kd,
                                               uint32_t* __restrict__ ws) {
@@ -296,13 +325,19 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
   // lane l fills slot l % 16 of chunk l / 16, so it fetches the group of 4
   // keys that the chunk's rotation puts in that slot.  Blocks past the
   // document are not copied; keys past it in the last block are stale and
-  // never read back (every loop below stops at the chunk's valid count).
+  // never counted (see read_chunk).
+  // Valid keys of this thread's chunk in block c.
+  auto nvalid = [&](int c) __attribute__((always_inline)) {
+    const int r = owner ? doc - (c * B + tid * kCompactChunk) : 0;
+    return r <= 0 ? 0 : (r >= kCompactChunk ? kCompactChunk : r);
+  };
   int cur = -1;
-  auto load_block = [&](int c) __attribute__((always_inline)) {
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Issues the copies of block c; returns how many this wave issued.
+  auto issue_block = [&](int c) __attribute__((always_inline)) {
     const int base = c * B;
-    __syncthreads();
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cc = (tid & 63) >> 4, j = tid & 15;
+    int issued = 0;
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it) {
       const int wb = it * (THREADS / kWave) + wv;  // this wave's 256-key block
@@ -311,32 +346,39 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
         const int t = 4 * wb + cc;  // the chunk (and owner thread) this lane's slot belongs to
         dma16(keys + base + i0 + cc * kCompactChunk + 4 * ((j - t) & 15),
               (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)sel_key_ptr(kp, i0));
+        ++issued;
       }
     }
+    return issued;
+  };
+  auto load_block = [&](int c) __attribute__((always_inline)) {
+    __syncthreads();  // the previous block's readers are done
+    issue_block(c);
     wait_vm<0>();
     __syncthreads();
     cur = c;
   };
-  // Valid keys of this thread's chunk in block c.
-  auto nvalid = [&](int c) __attribute__((always_inline)) {
-    const int r = owner ? doc - (c * B + tid * kCompactChunk) : 0;
-    return r <= 0 ? 0 : (r >= kCompactChunk ? kCompactChunk : r);
-  };
-  // All 64 keys of this thread's chunk (16 reads in flight).
-  auto read_chunk = [&](u32x4 (&k)[16]) __attribute__((always_inline)) {
+  // Padding keys (value 0): the tail of the chunk the document ends in.
+  const uint32_t pad_total = (uint32_t)((kCompactChunk - doc % kCompactChunk) % kCompactChunk);
+  // All 64 keys of this thread's chunk (16 reads in flight), those past the
+  // document's end set to 0 (only in the chunk the document ends in).
+  auto read_chunk = [&](u32x4 (&k)[16], int nv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) k[i] = *reinterpret_cast<const u32x4*>(slot_of(mine, tid, i));
+    if (nv < kCompactChunk) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) k[j >> 2][j & 3] = j < nv ? k[j >> 2][j & 3] : 0u;
+    }
   };
 
-  // ---- top digit: the published histogram (read past the L2), into LDS,
-  // with the first block's keys in flight at the same time.
-  uint32_t hc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) hc[i] = __hip_atomic_load(&ws[tid + i * THREADS], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  load_block(0);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) sh.hist[tid + i * THREADS] = hc[i];
-  __syncthreads();
+  // ---- top digit: the published histogram and the first block of keys,
+  // both by global -> LDS copies (the caller has dropped its L2's stale
+  // lines), the histogram first: waiting for it leaves the keys in flight
+  // while the top digit is resolved below.
+  static_assert(kSelBins * 4 == THREADS * 16, "one 16-byte copy of the histogram per thread");
+  dma16(ws + 4 * tid, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&sh.hist[0] + wv * 1024);
+  wait_vm_n<kMaxIt>(issue_block(0));
+  lds_barrier();
 
   // Phases over the blocks of keys, the current block kept in LDS between
   // phases: 0 counts the top digit again (only if the published counts do
@@ -360,52 +402,75 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
       }
     }
   }
+  // The first block's keys.
+  wait_vm<0>();
+  __syncthreads();
+  cur = 0;
   uint32_t* items = ws + sel_items_word(doc);
   uint32_t run_gt = 0, run_eq = 0, run_items = 0;
 #pragma unroll 1
   for (; phase < 4; ++phase) {
-    const int known = phase == 1 ? 11 : 22;
-    const int w = phase == 1 ? 11 : 10;
-    const int shift = 32 - known - w;
-    const uint32_t mask = (1u << w) - 1u;
     if (phase < 3) {
       for (int i = tid; i < kSelBins; i += THREADS) sh.hist[i] = 0u;
-      __syncthreads();
+      lds_barrier();
     }
 #pragma unroll 1
     for (int c = 0; c < nblocks; ++c) {
       if (c != cur) load_block(c);
       const int nv = nvalid(c);
+      const bool live = nv > 0;  // owns a chunk with document tokens in this block
       u32x4 k[16];
-      read_chunk(k);
-      // Keys past the chunk's valid count are masked off at the end, not
-      // tested one by one.
-      const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+      if (live) read_chunk(k, nv);
       if (phase < 3) {
-        // One predicated LDS atomic per key still in play, straight from the
-        // registers: a loop over the live keys alone would run as many rounds
-        // as the fullest chunk of the wave holds, each round waiting for an
-        // LDS read of its key (kept tokens cluster, so one chunk can hold many).
-        const int sh_known = phase == 0 ? 0 : 32 - known;
-        const uint32_t want = phase == 0 ? 0u : prefix;
-        const uint32_t shmask = phase == 0 ? 0u : 0xffffffffu;
+        // One LDS atomic per key, straight from the registers, for every key:
+        // a key not in play adds to its lane's sink word instead of a bin.  A
+        // predicated atomic would put a chain of exec-mask updates around
+        // every key, which the keys cannot overlap; a loop over the live keys
+        // alone would run as many rounds as the fullest chunk of the wave
+        // holds (kept tokens cluster, so one chunk can hold many).
+        uint32_t* const sink = &sh.sink[tid & (kWave - 1)];
+        auto pass = [&](auto ph) __attribute__((always_inline)) {
+          constexpr int P = decltype(ph)::value;
 #pragma unroll
-        for (int j = 0; j < 64; ++j) {
-          const uint32_t kk = k[j >> 2][j & 3];
-          if (j < nv && ((kk >> sh_known) & shmask) == want)
-            atomicAdd(&sh.hist[phase == 0 ? kk >> 21 : (kk >> shift) & mask], 1u);
+          for (int j = 0; j < 64; ++j) {
+            const uint32_t kk = k[j >> 2][j & 3];
+            if constexpr (P == 0) {
+              atomicAdd(&sh.hist[kk >> 21], 1u);
+            } else if constexpr (P == 1) {
+              atomicAdd((kk >> 21) == prefix ? &sh.hist[(kk >> 10) & 2047u] : sink, 1u);
+            } else {
+              atomicAdd((kk >> 10) == prefix ? &sh.hist[kk & 1023u] : sink, 1u);
+            }
+          }
+        };
+        if (live) {
+          if (phase == 1)
+            pass(std::integral_constant<int, 1>{});
+          else if (phase == 2)
+            pass(std::integral_constant<int, 2>{});
+          else
+            pass(std::integral_constant<int, 0>{});
         }
         continue;
       }
-      // phase 3: counts of this chunk, then block scans in chunk order.
-      uint64_t mgt = 0, meq = 0;
+      // phase 3: counts of this chunk, then block scans in chunk order.  With
+      // need == 0 no key equal to T is kept, and those counts are not needed
+      // (they are written as 0).
+      uint32_t cgt = 0, ceq = 0;
+      if (live) {
+        if (need == 0u) {
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const uint32_t kk = k[j >> 2][j & 3];
-        mgt |= (uint64_t)(kk > T) << j;
-        meq |= (uint64_t)(kk == T) << j;
+          for (int j = 0; j < 64; ++j) cgt += k[j >> 2][j & 3] > T ? 1u : 0u;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 64; ++j) {
+            const uint32_t kk = k[j >> 2][j & 3];
+            cgt += kk > T ? 1u : 0u;
+            ceq += kk == T ? 1u : 0u;
+          }
+          if (T == 0u) ceq -= (uint32_t)(kCompactChunk - nv);  // the padding keys
+        }
       }
-      const uint32_t cgt = (uint32_t)__popcll(mgt & valid), ceq = (uint32_t)__popcll(meq & valid);
       uint32_t gt_b, eq_b, tgt, teq, eni, tni, ni;
       if (need == 0u) {  // keys equal to T are never kept: the items follow from cgt alone
         ni = nv > 0 ? (cgt + kItemRows - 1) / kItemRows : 0u;
@@ -440,9 +505,13 @@ __device__ __forceinline__ void select_finish(SelFinishShared& sh, const SelKeys
       run_items += tni;
     }
     if (phase < 3) {
-      __syncthreads();
+      lds_barrier();
+      // The padding keys (0) were counted when this pass's prefix is 0: all
+      // of them in digit 0.
+      const bool pad_counted = phase == 0 || prefix == 0u;
       uint32_t bin, rest, cnt;
-      sel_resolve<THREADS>(sh, need, bin, rest, cnt);
+      sel_resolve<THREADS>(sh, need, bin, rest, cnt, nullptr, pad_counted ? pad_total : 0u);
+      const int w = phase == 1 ? 11 : 10;
       const int bits_left = phase == 0 ? 21 : (phase == 1 ? 10 : 0);
       prefix = phase == 0 ? bin : (prefix << w) | bin;
       need = rest;
