@@ -175,6 +175,30 @@ def test_select_ws_dirty_workspace_and_unaligned_scores(gpu_lib):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref_select(base[1:].numpy(), 3000, 16))
 
 
+@pytest.mark.parametrize("dirty", [False, True])
+@pytest.mark.parametrize("n,k,q", [(4097, 3600, 64), (30001, 27000, 1), (2113, 2000, 0)])
+def test_select_ws_nan_threshold_in_a_partial_chunk(gpu_lib, n, k, q, dirty):
+    """The kd-th largest document score is a NaN (so T is the key of NaN, 0) and
+    the document ends inside a 64-token chunk: the ranking treats the keys past
+    the document's end as that same key and must take them back out of every
+    count of it (histogram bin 0 of a zero prefix, and the count equal to T).
+    The workspace starts clean or full of garbage (this entry clears its
+    histogram itself), and the second call reuses what the first left."""
+    _say("select ws NaN threshold", n, k, q, "dirty" if dirty else "clean")
+    g = W.random_scores(n, 21)
+    g[::3] = float("nan")
+    g[1::10] = float("nan")
+    doc, kd = n - q, k - q
+    assert doc % 64 != 0 and int(torch.isnan(g[:doc]).logical_not().sum()) < kd  # the threshold is a NaN
+    size = gpu_lib.tg_select_topk_workspace_size(n)
+    ws = (torch.full((size,), 0xAB, dtype=torch.uint8, device=DEV) if dirty
+          else torch.zeros(size, dtype=torch.uint8, device=DEV))
+    for _ in range(2):  # the second call starts from the workspace the first left behind
+        idx = gpu_lib.tg_select_topk_ws(g.to(DEV), k, q, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_select(g.numpy(), k, q))
+
+
 def test_select_varlen_ragged_batch(gpu_lib):
     ns, qs = W.ragged_lengths(8, W.SEEDS["ragged8"])
     ns = ns[:6] + [100, 0]
@@ -282,6 +306,29 @@ def test_gate_select_recounts_a_histogram_that_does_not_add_up(gpu_lib):
     _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
     torch.cuda.synchronize()
     assert _counts_clean(ws)
+
+
+def test_gate_select_nan_threshold_with_a_stale_histogram(gpu_lib):
+    """Hidden states with NaN rows score NaN, the lowest rank.  With fewer finite
+    document scores than the budget, the threshold T is the key of NaN (0), the
+    key the ranking also gives to the positions past the document's end in its
+    last chunk (the document here ends 56 tokens into it).  A stale histogram
+    makes the last workgroup count the top digit from the keys itself; every
+    count of key 0 must leave those positions out."""
+    n, d, k, q = 20000, 256, 15000, 40
+    h = W.hidden_states(n, d, torch.bfloat16, 52)
+    h[::2] = float("nan")
+    w1, b1, w2, _ = W.gate_weights(d, 256, torch.bfloat16, 52)
+    for stale in (False, True):
+        _say("gate_select NaN threshold", "stale" if stale else "clean")
+        ws = gpu_lib.select_workspace(n, DEV)
+        if stale:
+            ws[:8192] = 7  # stale histogram words; the arrival counter stays zero
+        g = _gate_select_case(gpu_lib, h, w1, b1, w2, 0.0, k, q, ws=ws)
+        doc, kd = n - q, k - q
+        assert doc % 64 != 0 and int(np.isfinite(g[:doc]).sum()) < kd  # the threshold is a NaN
+        torch.cuda.synchronize()
+        assert _counts_clean(ws)
 
 
 def test_gate_select_fp32_tiny(gpu_lib):
