@@ -20,7 +20,8 @@
 //   [2050]      need, how many document keys equal to T are kept;
 //   [2051]      the number of copy items (below);
 //   [2112 + 2c] for each 64-token chunk c of the document: the number of its
-//               keys above T, then equal to T, in the chunks before it;
+//               keys above T, then equal to T, in the chunks before it (the
+//               second written as 0 when need is 0: no equal key is kept);
 //   then        copy items, chunk * 16 + part: part p of chunk c stands for
 //               the chunk's kept tokens of rank 8p .. 8p + 7 (at most 8
 //               rows per item, however the kept tokens cluster);
@@ -294,7 +295,8 @@ __device__ __forceinline__ bool sel_publish_and_arrive(SelFinishShared& sh, uint
 // bank groups); a document of several blocks is re-read once per pass.  A
 // single workgroup runs this once: each phase reads the thread's 64 keys into
 // registers with all its LDS reads in flight, then works from the registers
-// (a counting pass issues one predicated LDS atomic per key still in play).
+// (a counting pass issues one LDS atomic per key: to its bin if the key is
+// still in play, else to its lane's sink word).
 // Chunks wholly past the document take no part; in the one chunk the
 // document ends in, the keys past its end are set to 0 (the key of NaN) in
 // registers, so no pass tests a key's index; wherever a pass counts key 0
