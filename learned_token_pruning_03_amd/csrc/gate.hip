@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
   // pairs of quads (xor 2), mirrored half-rows and mirrored rows leave the
   // row's sum in all its lanes; then every row adds lane 15 of the row before
   // it (row_bcast:15), so lanes 31 and 63 hold the sums of their halves.  Each
-  // step is one add with a DPP source; a shuffle per step would go through
-  // the LDS and wait for it.
+  // step is an add with a DPP source (the broadcast a DPP move and an add); a
+  // shuffle per step would go through the LDS and wait for it.
   auto dpp_add = [](float v, auto ctrl_tag) __attribute__((always_inline)) {
     constexpr int ctrl = decltype(ctrl_tag)::value;
     return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
