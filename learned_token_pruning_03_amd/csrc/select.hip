@@ -408,10 +408,12 @@ __device__ __forceinline__ ChunkLane decide_chunk(const CompactArgs& a, int c, i
   const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
   const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
   const uint32_t eq_rank = eq_b + pe;
-  r.slot = in_doc ? (int)(gt_b + pg + min(eq_rank, need)) : a.kd + (r.j - a.doc);
-  // A slot outside the document's range only comes from a workspace that
-  // does not hold this call's counts: nothing is written for it.
-  r.kept = in_tail || ((gt || (eq && eq_rank < need)) && r.slot < a.kd);
+  const uint32_t doc_slot = gt_b + pg + min(eq_rank, need);
+  r.slot = in_doc ? (int)doc_slot : a.kd + (r.j - a.doc);
+  // A slot outside [0, kd) only comes from a workspace that does not hold
+  // this call's counts: nothing is written for it (compared unsigned, so
+  // counts that wrap past 2^31 cannot give a negative slot either).
+  r.kept = in_tail || ((gt || (eq && eq_rank < need)) && doc_slot < (uint32_t)a.kd);
   return r;
 }
 
@@ -450,6 +452,9 @@ __global__ __launch_bounds__(256) void gather_items_kernel(CompactArgs a) {
     const int item = b - a.tail_items;
     if (item >= (int)a.ws[kSelWsItems]) return;
     const uint32_t code = a.ws[sel_items_word(a.doc) + item];
+    // A chunk past the document only comes from a workspace that does not
+    // hold this call's item list: nothing is read or written for it.
+    if ((code >> 4) >= (uint32_t)sel_chunks(a.doc)) return;
     const int c = (int)(code >> 4), part = (int)(code & 15u);
     if (wave == 0) {
       const ChunkLane r = decide_chunk(a, c, lane);
