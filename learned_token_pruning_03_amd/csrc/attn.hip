@@ -448,39 +448,59 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
               sacc[mb][4 * rq + e] = j > qi ? -INFINITY : sacc[mb][4 * rq + e];
             }
       }
-      float mloc = -INFINITY;
+      // p = 2^(c*s - m) against the lane's reference maximum m, packed to
+      // bf16 for the PV product; returns the lane's sum of p (four partial
+      // sums, so the adds do not form one serial chain).
+      auto weights = [&]() __attribute__((always_inline)) {
+        const float msub = (m == -INFINITY) ? 0.0f : m;
+        float ps[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int kb = 0; kb < 4; ++kb) {
+          ps[kb] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mb][r]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float m_new = fmaxf(m, mloc * c);
-      // The reference maximum only moves when some lane's logits exceed it by
-      // more than 8 (log2 units); until then p <= 256, which the fp32
-      // accumulators and bf16 weights hold as well as p <= 1, and numerator
-      // and denominator share the shift.
-      if (__any(m_new > m + 8.0f)) {
-        const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-        m = m_new;
-      }
-      const float msub = (m == -INFINITY) ? 0.0f : m;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + e], c, -msub));
-          psum += p;
-          pf[kb][e] = (__bf16)p;
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + e], c, -msub));
+            ps[kb] += p;
+            pf[kb][e] = (__bf16)p;
+          }
         }
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      };
+      // The reference maximum is set from the row maxima on a wave's first
+      // tile and afterwards only when a tile's weights show it too low: some
+      // weight above 2^16, or a sum that overflowed or is NaN.  Until then
+      // every p stays below 2^16, which the fp32 sums and the bf16 weights
+      // hold with the same relative precision as p <= 1 (numerator and
+      // denominator share the shift), so the row maxima are not needed.
+      // When the check fails the tile is redone against its true maxima.
+      float psum = 0.0f;
+      bool exact = t == 0;
+      if (!exact) {
+        psum = weights();
+        exact = __any(!(psum <= 65536.0f));
+      }
+      if (exact) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mb][r]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_new = fmaxf(m, mloc * c);
+        if (__any(m_new > m)) {
+          const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+          lsum *= alpha;
+#pragma unroll
+          for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+          m = m_new;
+        }
+        psum = weights();
+      }
       lsum += psum;
     };
 

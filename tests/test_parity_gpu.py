@@ -491,6 +491,41 @@ def test_attn_bf16_shapes(gpu_lib, n, hq, hkv, dh, gkind):
     assert np.max(np.abs(lse - wl)) <= 1e-3
 
 
+def _rising_logit_inputs(n, hq, hkv, dh, seed, jump_at):
+    """Q/K whose logits spread over several units and grow along the prompt
+    (key j scaled by 1 + 3j/n), plus one key at jump_at sharing a direction
+    with every query so that its logit stands ~250 (natural units, > 128 in
+    base 2) above the others for all later queries: the running reference
+    maximum of the kernel has to move many times, once by more than the fp32
+    range of 2^x."""
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn(n, hq, dh, generator=gen, dtype=torch.float64) * 2.0
+    k = torch.randn(n, hkv, dh, generator=gen, dtype=torch.float64) * 2.0
+    v = torch.randn(n, hkv, dh, generator=gen, dtype=torch.float64) / dh ** 0.5
+    k *= (1.0 + 3.0 * torch.arange(n, dtype=torch.float64) / n)[:, None, None]
+    u = torch.zeros(dh, dtype=torch.float64)
+    u[: dh // 2] = 1.0
+    q += 2.0 * u
+    k[jump_at] = 250.0 * dh ** 0.5 / (2.0 * float(u @ u)) * u
+    pos = torch.arange(n, dtype=torch.int32)
+    bf = lambda x: x.to(torch.bfloat16).contiguous()
+    return bf(q), bf(k), bf(v), W.random_scores(n, seed), pos
+
+
+@pytest.mark.parametrize("n,hq,hkv,dh,jump_at", [(1000, 4, 2, 128, 517), (700, 4, 4, 64, 130)])
+def test_attn_bf16_rising_logits(gpu_lib, n, hq, hkv, dh, jump_at):
+    _say("attn bf16 rising logits", n, hq, hkv, dh, jump_at)
+    q, k, v, g, pos = _rising_logit_inputs(n, hq, hkv, dh, 77 + n, jump_at)
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    wo, wl = ref_attn(q, k, v, g, pos.numpy())
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err = float(np.max(np.abs(o - wo)))
+    _say("  max abs err o", err, "lse", float(np.max(np.abs(lse - wl))))
+    assert err <= 2e-2
+    # lse reaches ~400 here: fp32 keeps it to a few 1e-5.
+    assert np.max(np.abs(lse - wl)) <= 1e-3
+
+
 @pytest.mark.parametrize("n,hq,hkv,dh", [(200, 4, 2, 64), (77, 2, 1, 128)])
 def test_attn_fp32_shapes(gpu_lib, n, hq, hkv, dh):
     q, k, v, g, pos = _attn_inputs(n, hq, hkv, dh, torch.float32, n, "edge")
