@@ -31,9 +31,10 @@
 //    the normalised output tile leaves through LDS as whole rows, so no load
 //    or store instruction touches 32 query rows at once;
 //  * the causal test runs only on tiles reaching past a wave's first query;
-//  * the online softmax keeps a reference maximum per query that only moves
-//    when a logit exceeds it by more than 8 (log2 units), so the O rescale is
-//    skipped on almost every tile;
+//  * the online softmax takes row maxima only on a wave's first tile; later
+//    tiles reuse that reference maximum until a tile's weight sum shows a
+//    weight above 2^16 (or overflow), and only then are the maxima taken and
+//    O rescaled, so almost every tile skips both;
 //  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
 //    the same XCD, where they share that head's K/V in L2.
 //  * a workgroup owns a pair of query tiles, (T-1-p) then p, so every
