@@ -33,7 +33,7 @@
 //  * the causal test runs only on tiles reaching past a wave's first query;
 //  * the online softmax takes row maxima only on a wave's first tile; later
 //    tiles reuse that reference maximum until a tile's weight sum shows a
-//    weight above 2^16 (or overflow), and only then are the maxima taken and
+//    weight above 2^64 (or overflow), and only then are the maxima taken and
 //    O rescaled, so almost every tile skips both;
 //  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
 //    the same XCD, where they share that head's K/V in L2.
@@ -469,16 +469,18 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       };
       // The reference maximum is set from the row maxima on a wave's first
       // tile and afterwards only when a tile's weights show it too low: some
-      // weight above 2^16, or a sum that overflowed or is NaN.  Until then
-      // every p stays below 2^16, which the fp32 sums and the bf16 weights
-      // hold with the same relative precision as p <= 1 (numerator and
-      // denominator share the shift), so the row maxima are not needed.
-      // When the check fails the tile is redone against its true maxima.
+      // weight above 2^64, or a sum that overflowed or is NaN.  Until then
+      // every p stays below 2^64: the fp32 sums, the bf16 weights and the O
+      // accumulators keep the same relative precision as with p <= 1
+      // (numerator and denominator share the shift) and stay far from the
+      // fp32 range, so the row maxima are not needed.  When the check fails
+      // the tile is redone against its true maxima.
+      constexpr float kWeightBound = 18446744073709551616.0f;  // 2^64
       float psum = 0.0f;
       bool exact = t == 0;
       if (!exact) {
         psum = weights();
-        exact = __any(!(psum <= 65536.0f));
+        exact = __any(!(psum <= kWeightBound));
       }
       if (exact) {
         float mloc = -INFINITY;

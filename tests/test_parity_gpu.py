@@ -491,13 +491,14 @@ def test_attn_bf16_shapes(gpu_lib, n, hq, hkv, dh, gkind):
     assert np.max(np.abs(lse - wl)) <= 1e-3
 
 
-def _rising_logit_inputs(n, hq, hkv, dh, seed, jump_at):
+def _rising_logit_inputs(n, hq, hkv, dh, seed, jump_at, jump=250.0):
     """Q/K whose logits spread over several units and grow along the prompt
     (key j scaled by 1 + 3j/n), plus one key at jump_at sharing a direction
-    with every query so that its logit stands ~250 (natural units, > 128 in
-    base 2) above the others for all later queries: the running reference
-    maximum of the kernel has to move many times, once by more than the fp32
-    range of 2^x."""
+    with every query so that its logit is about `jump` (natural units) for
+    all later queries.  jump = 250 puts it more than 128 base-2 units above
+    every earlier key (past the fp32 range of 2^x); jump = 90 puts it 64 to
+    128 units above them (weights finite but past 2^64).  Either way the
+    kernel's reference maximum must move."""
     gen = torch.Generator().manual_seed(seed)
     q = torch.randn(n, hq, dh, generator=gen, dtype=torch.float64) * 2.0
     k = torch.randn(n, hkv, dh, generator=gen, dtype=torch.float64) * 2.0
@@ -506,16 +507,17 @@ def _rising_logit_inputs(n, hq, hkv, dh, seed, jump_at):
     u = torch.zeros(dh, dtype=torch.float64)
     u[: dh // 2] = 1.0
     q += 2.0 * u
-    k[jump_at] = 250.0 * dh ** 0.5 / (2.0 * float(u @ u)) * u
+    k[jump_at] = jump * dh ** 0.5 / (2.0 * float(u @ u)) * u
     pos = torch.arange(n, dtype=torch.int32)
     bf = lambda x: x.to(torch.bfloat16).contiguous()
     return bf(q), bf(k), bf(v), W.random_scores(n, seed), pos
 
 
-@pytest.mark.parametrize("n,hq,hkv,dh,jump_at", [(1000, 4, 2, 128, 517), (700, 4, 4, 64, 130)])
-def test_attn_bf16_rising_logits(gpu_lib, n, hq, hkv, dh, jump_at):
-    _say("attn bf16 rising logits", n, hq, hkv, dh, jump_at)
-    q, k, v, g, pos = _rising_logit_inputs(n, hq, hkv, dh, 77 + n, jump_at)
+@pytest.mark.parametrize("n,hq,hkv,dh,jump_at,jump", [(1000, 4, 2, 128, 517, 250.0), (700, 4, 4, 64, 130, 250.0),
+                                                    (1000, 4, 2, 128, 517, 90.0)])
+def test_attn_bf16_rising_logits(gpu_lib, n, hq, hkv, dh, jump_at, jump):
+    _say("attn bf16 rising logits", n, hq, hkv, dh, jump_at, jump)
+    q, k, v, g, pos = _rising_logit_inputs(n, hq, hkv, dh, 77 + n, jump_at, jump)
     o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
     wo, wl = ref_attn(q, k, v, g, pos.numpy())
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
