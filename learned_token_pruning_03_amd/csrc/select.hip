@@ -388,15 +388,15 @@ struct ChunkLane {
   int slot;
 };
 
-__device__ __forceinline__ ChunkLane decide_chunk(const CompactArgs& a, int c, int lane) {
+// T and need are the ranking's threshold key and the count of tokens equal to
+// it to keep (passed in, so callers can load them early).
+__device__ __forceinline__ ChunkLane decide_chunk(const CompactArgs& a, int c, int lane, uint32_t T, uint32_t need) {
   ChunkLane r;
   r.j = c * kCompactChunk + lane;
   const bool in_doc = r.j < a.doc;
   const bool in_tail = !in_doc && r.j < a.n;
   r.gj = (r.j < a.n) ? a.g[r.j] : 0.0f;
   const uint32_t key = order_key(r.gj);
-  const uint32_t T = a.ws[kSelWsT];
-  const uint32_t need = a.ws[kSelWsNeed];
   uint32_t gt_b = 0, eq_b = 0;
   if (c * kCompactChunk < a.doc) {
     gt_b = a.ws[kSelWsChunks + 2 * c];
@@ -419,7 +419,7 @@ __device__ __forceinline__ ChunkLane decide_chunk(const CompactArgs& a, int c, i
 
 // Indices only: one wave per 64-token chunk of [0, n).
 __global__ __launch_bounds__(64) void compact_kernel(CompactArgs a) {
-  const ChunkLane r = decide_chunk(a, blockIdx.x, threadIdx.x);
+  const ChunkLane r = decide_chunk(a, blockIdx.x, threadIdx.x, a.ws[kSelWsT], a.ws[kSelWsNeed]);
   if (r.kept) a.idx[r.slot] = r.j;
 }
 
@@ -450,14 +450,20 @@ __global__ __launch_bounds__(256) void gather_items_kernel(CompactArgs a) {
     }
   } else {
     const int item = b - a.tail_items;
-    if (item >= (int)a.ws[kSelWsItems]) return;
+    // The item count, this item's code and the threshold are loaded together
+    // rather than one after another: the grid has sel_max_items(doc) item
+    // workgroups, so the code slot lies in the workspace for each of them
+    // (the code of an item past the count is never used).
+    const uint32_t count = a.ws[kSelWsItems];
     const uint32_t code = a.ws[sel_items_word(a.doc) + item];
+    const uint32_t T = a.ws[kSelWsT], need = a.ws[kSelWsNeed];
+    if (item >= (int)count) return;
     // A chunk past the document only comes from a workspace that does not
     // hold this call's item list: nothing is read or written for it.
     if ((code >> 4) >= (uint32_t)sel_chunks(a.doc)) return;
     const int c = (int)(code >> 4), part = (int)(code & 15u);
     if (wave == 0) {
-      const ChunkLane r = decide_chunk(a, c, lane);
+      const ChunkLane r = decide_chunk(a, c, lane, T, need);
       const uint64_t bk = __ballot(r.kept);
       const int kr = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u));
       const int lo = part * kItemRows;

@@ -767,6 +767,50 @@ def test_end_to_end_qwen_32k(gpu_lib):
     assert np.max(np.abs(lse.cpu().double().numpy()[:, rows] - wl)) <= 1e-3
 
 
+def test_end_to_end_stack19_fused_calls(gpu_lib):
+    """The 19-layer stack workload through the calls of its timed step: the
+    fused gate + select + gather on the 65536-token prompt, then for each of
+    the 19 upper layers RoPE + KV and gated attention with that layer's own
+    q, k, v (drawn from seed * 1000 + layer).  The kept rows, gate values and
+    positions are bit-exact against the oracle's select and gather on the g the
+    call wrote; every layer's rotated q and its attention (sampled query rows,
+    all heads) are checked against the oracle."""
+    tg = gpu_lib
+    sh = W.SHAPES["stack19"]
+    seed = W.SEEDS["stack19"]
+    _say("end-to-end stack19", sh.n, sh.k, sh.layers)
+    h = W.hidden_states(sh.n, sh.d, sh.dtype, seed, planted_frac=sh.planted_frac)
+    w1, b1, w2, b2 = W.gate_weights(sh.d, sh.hidden, sh.dtype, seed)
+    ws = tg.select_workspace(sh.n, DEV)
+    g, idx, hk, gk, pos = tg.tg_gate_select_gather(h.to(DEV), w1.to(DEV), b1.to(DEV), w2.to(DEV), b2, sh.k,
+                                                   sh.q_len, workspace=ws)
+    table = tg.tg_rope_table(sh.n, sh.dh, sh.rope_base, DEV)
+    torch.cuda.synchronize()
+    g_cpu = g.cpu().numpy()
+    idx_ref = ref_select(g_cpu, sh.k, sh.q_len)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    wh, wg, wp = ref_gather(h.view(torch.int16).numpy(), g_cpu, idx_ref)
+    np.testing.assert_array_equal(hk.cpu().view(torch.int16).numpy(), wh)
+    np.testing.assert_array_equal(gk.cpu().numpy(), wg)
+    np.testing.assert_array_equal(pos.cpu().numpy(), wp)
+    rows = _sample_rows(sh.k, 19, count=24)
+    worst = 0.0
+    for layer in range(sh.layers):
+        q, k, v = W.qkv(sh.k, sh.hq, sh.hkv, sh.dh, sh.qkv_var, sh.dtype, seed * 1000 + layer)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        _, kc, vc = tg.tg_rope_kv(qd, kd, vd, pos, table)
+        o, lse = tg.tg_gated_attn(qd, kc, vc, gk, pos, want_lse=True)
+        torch.cuda.synchronize()
+        rq = ref_rope(q, wp, sh.rope_base)
+        assert np.all(np.abs(qd.cpu().double().numpy() - rq) <= 2.0 ** -8 * np.abs(rq) + 1e-6), layer
+        wo, wl = ref_attn(qd.cpu(), kc.cpu(), vc.cpu(), wg, wp, rows=rows)
+        err = float(np.max(np.abs(o.cpu().double().numpy()[rows] - wo)))
+        worst = max(worst, err)
+        assert err <= 2e-2, (layer, err)
+        assert np.max(np.abs(lse.cpu().double().numpy()[:, rows] - wl)) <= 1e-3, layer
+    _say("  worst max abs err o over 19 layers", worst)
+
+
 def test_repeat_runs_are_bitwise_identical(gpu_lib):
     """Ten runs of every stage on the same inputs give the same bytes: the gate,
     both selects (the multi-workgroup one builds its histograms with device
