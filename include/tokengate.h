@@ -66,8 +66,8 @@ typedef enum tg_status {
   TG_OK = 0,
   TG_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, inconsistent sizes */
   TG_ERR_UNSUPPORTED = 2, /* valid request that this build has no kernel for */
-  TG_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
-  TG_ERR_WORKSPACE = 4    /* caller workspace smaller than its size function asks for */
+  TG_ERR_WORKSPACE = 3,   /* caller workspace smaller than its size function asks for */
+  TG_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } tg_status;
 
 typedef enum tg_dtype {

@@ -44,7 +44,8 @@ def test_status_strings_and_version(lib):
     assert lib.tg_abi_version() == 1
     assert tg.status_string(0) == "TG_OK"
     assert tg.status_string(1) == "TG_ERR_INVALID_ARG"
-    assert tg.status_string(4) == "TG_ERR_WORKSPACE"
+    assert tg.status_string(3) == "TG_ERR_WORKSPACE"
+    assert tg.status_string(4) == "TG_ERR_HIP"
     assert tg.status_string(99) == "TG_UNKNOWN_STATUS"
 
 
