@@ -474,13 +474,16 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       // accumulators keep the same relative precision as with p <= 1
       // (numerator and denominator share the shift) and stay far from the
       // fp32 range, so the row maxima are not needed.  When the check fails
-      // the tile is redone against its true maxima.
+      // the tile is redone against its true maxima.  A lane with no reference
+      // yet (no visible key in its first tile) must see no weight either:
+      // such a lane never meets a visible key later (its group's first tile
+      // covers its earliest keys), and the check makes sure of it.
       constexpr float kWeightBound = 18446744073709551616.0f;  // 2^64
       float psum = 0.0f;
       bool exact = t == 0;
       if (!exact) {
         psum = weights();
-        exact = __any(!(psum <= kWeightBound));
+        exact = __any(!(psum <= kWeightBound) || (psum > 0.0f && m == -INFINITY));
       }
       if (exact) {
         float mloc = -INFINITY;
