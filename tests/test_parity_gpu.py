@@ -528,6 +528,23 @@ def test_attn_bf16_rising_logits(gpu_lib, n, hq, hkv, dh, jump_at, jump):
     assert np.max(np.abs(lse - wl)) <= 1e-3
 
 
+def test_attn_bf16_rising_logits_streamed_bias(gpu_lib):
+    """The same redo path in the streamed-bias form (8300 keys, past the LDS
+    bias table at head dim 128), on sampled query rows that include the rows
+    around the planted key."""
+    n, jump_at = 8300, 5003
+    _say("attn bf16 rising logits, streamed bias", n)
+    q, k, v, g, pos = _rising_logit_inputs(n, 2, 1, 128, 91, jump_at)
+    o, lse = _run_attn(gpu_lib, q, k, v, g, pos)
+    rows = np.unique(np.concatenate([_sample_rows(n, 9, count=40), np.arange(jump_at - 2, jump_at + 3)]))
+    wo, wl = ref_attn(q, k, v, g, pos.numpy(), rows=rows)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err = float(np.max(np.abs(o[rows] - wo)))
+    _say("  max abs err o", err)
+    assert err <= 2e-2
+    assert np.max(np.abs(lse[:, rows] - wl)) <= 1e-3
+
+
 @pytest.mark.parametrize("n,hq,hkv,dh", [(200, 4, 2, 64), (77, 2, 1, 128)])
 def test_attn_fp32_shapes(gpu_lib, n, hq, hkv, dh):
     q, k, v, g, pos = _attn_inputs(n, hq, hkv, dh, torch.float32, n, "edge")
