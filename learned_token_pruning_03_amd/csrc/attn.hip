@@ -33,8 +33,9 @@
 //  * the causal test runs only on tiles reaching past a wave's first query;
 //  * the online softmax takes row maxima only on a wave's first tile; later
 //    tiles reuse that reference maximum until a tile's weight sum shows a
-//    weight above 2^64 (or overflow), and only then are the maxima taken and
-//    O rescaled, so almost every tile skips both;
+//    weight above 2^64 (or overflow); that tile is redone against its row
+//    maxima, and the wave then takes them on every tile, moving its
+//    reference only when a logit exceeds it by more than 8 (log2 units);
 //  * blockIdx -> (KV head, query head) puts all query heads of one KV head on
 //    the same XCD, where they share that head's K/V in L2.
 //  * a workgroup owns a pair of query tiles, (T-1-p) then p, so every
@@ -320,6 +321,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
     };
 
     float m = -INFINITY;
+    bool eager = false;  // this wave takes the row maxima on every tile (see the VALU slot)
     float lsum = 0.0f;
     f32x16 oacc[C::MD];
 #pragma unroll
@@ -474,18 +476,26 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
       // accumulators keep the same relative precision as with p <= 1
       // (numerator and denominator share the shift) and stay far from the
       // fp32 range, so the row maxima are not needed.  When the check fails
-      // the tile is redone against its true maxima.  A lane with no reference
-      // yet (no visible key in its first tile) must see no weight either:
-      // such a lane never meets a visible key later (its group's first tile
-      // covers its earliest keys), and the check makes sure of it.
+      // the tile is redone against its true maxima, and from then on the wave
+      // takes the row maxima on every tile (logits that outgrow the first
+      // tile's maxima that far tend to keep rising, and each redo computes
+      // the tile's weights twice).  A lane with no reference yet (no visible
+      // key in its first tile) must see no weight either: such a lane never
+      // meets a visible key later (its group's first tile covers its earliest
+      // keys), and the check makes sure of it.
       constexpr float kWeightBound = 18446744073709551616.0f;  // 2^64
       float psum = 0.0f;
-      bool exact = t == 0;
+      bool exact = t == 0 || eager;
       if (!exact) {
         psum = weights();
         exact = __any(!(psum <= kWeightBound) || (psum > 0.0f && m == -INFINITY));
+        eager = exact;
       }
       if (exact) {
+        // The reference moves only when some lane's logits exceed it by more
+        // than 8 (log2 units): weights stay below 2^8, and the O rescale is
+        // skipped on most tiles.  A tile that failed the check always moves
+        // it (some weight was above 2^64), and so does the first (m = -inf).
         float mloc = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(AttnArgs a) {
           mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
         const float m_new = fmaxf(m, mloc * c);
-        if (__any(m_new > m)) {
+        if (__any(m_new > m + 8.0f)) {
           const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
           lsum *= alpha;
 #pragma unroll
