@@ -416,6 +416,10 @@ def upper_layer(tg, W, sh, dev, m, gated, reps=8):
     import torch
     d, hq, hkv, dh = sh.d, sh.hq, sh.hkv, sh.dh
     x = W.hidden_states(m, d, sh.dtype, 21).to(dev)
+    # The O and down projections add into x in place; every repetition starts
+    # from the same x again (restored outside the timed stages), so each one
+    # times one layer pass on the same input.
+    x0 = x.clone()
     w_qkv = W.linear_weight((hq + 2 * hkv) * dh, d, sh.dtype, 22).to(dev)
     w_o = W.linear_weight(d, hq * dh, sh.dtype, 23).to(dev)
     w_g = W.linear_weight(FFN, d, sh.dtype, 24).to(dev)
@@ -444,6 +448,7 @@ def upper_layer(tg, W, sh, dev, m, gated, reps=8):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
     times = {n: [] for n, _ in stages}
     for r in range(reps + 1):
+        x.copy_(x0)
         queue_ahead(torch)
         ev[0].record()
         for i, (_, fn) in enumerate(stages):
